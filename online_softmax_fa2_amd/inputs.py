@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the attention, decode and row-softmax workloads.
+
+This module is shared by the GPU tests, the benchmark and the CPU oracle's
+tests, so it deliberately holds none of the method's arithmetic: only random
+draws, the round-to-nearest-even conversion of inputs to bfloat16, the
+scaling of a fixed key subset by 8 (exact in bfloat16) and the workload
+shapes.  Nothing here computes a score, a maximum, an exponential or a sum.
+
+Recipe (every draw is reproducible from the seed list alone):
+  * attention: for each (b, h) slice, ``numpy.random.default_rng([seed, b, h])``
+    draws Q, K, V in that order with ``standard_normal(dtype=float32)``;
+  * extra draws (the key subset that is scaled by 8) use
+    ``default_rng([seed, 1000])``;
+  * row softmax: ``default_rng([seed, r // 256])`` draws blocks of 256 rows of
+    ``standard_normal(float32)`` which are multiplied by the workload's sigma
+    (4, a power of two, so the product is exact).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bfloat16 conversion of inputs (host side, round to nearest even)
+# ---------------------------------------------------------------------------
+
+
+def bf16_round(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Round finite float32 values to bfloat16, ties to even.
+
+    Returns ``(bits, values)``: the bfloat16 bit patterns as uint16 and the
+    same numbers widened back to float32 (exactly representable).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    bits = ((u + bias) >> 16).astype(np.uint16)
+    values = (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits, values
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 values exactly."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Attention inputs
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class AttnInputs:
+    """Q, K, V as float32 values (bf16-representable when dtype == 'bf16')."""
+
+    q: np.ndarray  # [B, H, N, d] float32
+    k: np.ndarray
+    v: np.ndarray
+    dtype: str  # 'f32' or 'bf16'
+    scale: float  # the float32 scale the library receives
+    causal: bool = False
+    window: int = 0
+    kv_len: np.ndarray | None = None  # [B] int32 or None
+    big_keys: np.ndarray | None = None  # key positions scaled by 8, if any
+    q_bits: np.ndarray | None = field(default=None, repr=False)  # uint16 when bf16
+    k_bits: np.ndarray | None = field(default=None, repr=False)
+    v_bits: np.ndarray | None = field(default=None, repr=False)
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded once to float32."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def attn_inputs(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", seed: int = 0,
+                causal: bool = False, window: int = 0, kv_len=None,
+                n_big_keys: int = 0, scale: float | None = None,
+                q_shift: float = 0.0, k_shift: float = 0.0, std: float = 1.0) -> AttnInputs:
+    """Draw Q, K, V of shape [B, H, N, d] from N(0, std^2) per (b, h) slice.
+
+    ``n_big_keys`` key positions (shared by all batches and heads, drawn
+    without replacement from ``default_rng([seed, 1000])``) are multiplied by
+    8 after rounding, which is exact in bfloat16.  ``q_shift``/``k_shift``
+    add a constant to every element before rounding (used to build rows whose
+    scores sit far from zero).
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    shape = (B, H, N, d)
+    q = np.empty(shape, np.float32)
+    k = np.empty(shape, np.float32)
+    v = np.empty(shape, np.float32)
+    for b in range(B):
+        for h in range(H):
+            rng = np.random.default_rng([seed, b, h])
+            q[b, h] = rng.standard_normal((N, d), dtype=np.float32) * np.float32(std) + np.float32(q_shift)
+            k[b, h] = rng.standard_normal((N, d), dtype=np.float32) * np.float32(std) + np.float32(k_shift)
+            v[b, h] = rng.standard_normal((N, d), dtype=np.float32) * np.float32(std)
+    out = AttnInputs(q=q, k=k, v=v, dtype=dtype,
+                     scale=default_scale(d) if scale is None else float(np.float32(scale)),
+                     causal=causal, window=window)
+    if dtype == "bf16":
+        out.q_bits, out.q = bf16_round(q)
+        out.k_bits, out.k = bf16_round(k)
+        out.v_bits, out.v = bf16_round(v)
+    if n_big_keys:
+        pos = np.sort(np.random.default_rng([seed, 1000]).choice(N, size=n_big_keys, replace=False))
+        out.big_keys = pos
+        out.k[:, :, pos, :] *= np.float32(8.0)
+        if dtype == "bf16":
+            out.k_bits, _ = bf16_round(out.k)  # exact: a power-of-two multiple
+    if kv_len is not None:
+        out.kv_len = np.asarray(kv_len, dtype=np.int32).reshape(B)
+    return out
+
+
+def decode_inputs(B: int, H: int, Nkv: int, d: int, *, seed: int = 0, dtype: str = "bf16"):
+    """One query per (b, h) plus K, V of length Nkv; same per-slice recipe."""
+    q = np.empty((B, H, d), np.float32)
+    k = np.empty((B, H, Nkv, d), np.float32)
+    v = np.empty((B, H, Nkv, d), np.float32)
+    for b in range(B):
+        for h in range(H):
+            rng = np.random.default_rng([seed, b, h])
+            q[b, h] = rng.standard_normal(d, dtype=np.float32)
+            k[b, h] = rng.standard_normal((Nkv, d), dtype=np.float32)
+            v[b, h] = rng.standard_normal((Nkv, d), dtype=np.float32)
+    res = {"q": q, "k": k, "v": v, "dtype": dtype}
+    if dtype == "bf16":
+        for name in ("q", "k", "v"):
+            bits, vals = bf16_round(res[name])
+            res[name] = vals
+            res[name + "_bits"] = bits
+    return res
+
+
+def decode_slice(seed: int, b: int, h: int, Nkv: int, d: int, dtype: str = "bf16"):
+    """The (b, h) slice of :func:`decode_inputs`, drawn on its own (bounded memory)."""
+    rng = np.random.default_rng([seed, b, h])
+    q = rng.standard_normal(d, dtype=np.float32)
+    k = rng.standard_normal((Nkv, d), dtype=np.float32)
+    v = rng.standard_normal((Nkv, d), dtype=np.float32)
+    if dtype == "bf16":
+        qb, q = bf16_round(q)
+        kb, k = bf16_round(k)
+        vb, v = bf16_round(v)
+        return q, k, v, qb, kb, vb
+    return q, k, v, None, None, None
+
+
+def softmax_rows_inputs(rows: int, cols: int, *, seed: int = 0, sigma: float = 4.0) -> np.ndarray:
+    """x[rows, cols] float32, i.i.d. N(0, sigma^2), drawn in blocks of 256 rows."""
+    x = np.empty((rows, cols), np.float32)
+    for r0 in range(0, rows, 256):
+        r1 = min(rows, r0 + 256)
+        rng = np.random.default_rng([seed, r0 // 256])
+        x[r0:r1] = rng.standard_normal((r1 - r0, cols), dtype=np.float32) * np.float32(sigma)
+    return x
+
+
+# ---------------------------------------------------------------------------
+# The five workloads (shapes, masks, seeds)
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {
+    # FP32 attention, N not a multiple of any tile, no mask.
+    "attn_f32_b1h1_n1000_d64": dict(kind="attn", B=1, H=1, N=1000, d=64, dtype="f32",
+                                     causal=False, window=0, kv_len=None, n_big_keys=0, seed=1),
+    # Row softmax and the fused top-5 variant, N(0, 4^2).
+    "softmax_rows_4096x4000": dict(kind="softmax", rows=4096, cols=4000, sigma=4.0, seed=2),
+    "softmax_top5_1024x25000": dict(kind="topk", rows=1024, cols=25000, k=5, sigma=4.0, seed=20),
+    # bf16 causal attention.
+    "attn_bf16_causal_b4h32_n2048_d128": dict(kind="attn", B=4, H=32, N=2048, d=128, dtype="bf16",
+                                               causal=True, window=0, kv_len=None, n_big_keys=0, seed=3),
+    # bf16 causal + sliding window 1024 + last 512 keys padded; 1% of keys x8.
+    "attn_bf16_causal_w1024_pad512_b1h64_n8192_d128": dict(
+        kind="attn", B=1, H=64, N=8192, d=128, dtype="bf16", causal=True, window=1024,
+        kv_len=[8192 - 512], n_big_keys=82, seed=4),
+    # Split-KV decode: one query per head, 131072 keys, 64 splits.
+    "decode_bf16_b1h32_nkv131072_d128_split64": dict(kind="decode", B=1, H=32, Nkv=131072, d=128,
+                                                      nsplit=64, dtype="bf16", seed=5),
+}
+
+
+def workload_attn_inputs(name: str, **override) -> AttnInputs:
+    w = dict(WORKLOADS[name])
+    w.update(override)
+    return attn_inputs(w["B"], w["H"], w["N"], w["d"], dtype=w["dtype"], seed=w["seed"],
+                       causal=w["causal"], window=w["window"], kv_len=w["kv_len"],
+                       n_big_keys=w["n_big_keys"])
