@@ -1,0 +1,14 @@
+"""online_softmax_fa2_amd -- exact softmax attention by the online-softmax
+recurrence, hand-written in HIP for AMD MI355X (gfx950).
+
+The compute path is the C-ABI library ``_lib/libosfa.so`` (sources in
+``csrc/``, declarations in ``include/osfa.h``); the functions exported here
+only marshal PyTorch tensors and streams into it.  Importing this package
+does not load the library; the first call does, and raises if it is not
+built.
+"""
+from ._binding import (OsfaError, attn_decode_splitkv, attn_fwd, decode_workspace_bytes,  # noqa: F401
+                       load_library, online_softmax_rows, online_softmax_topk_rows)
+
+__all__ = ["attn_fwd", "attn_decode_splitkv", "decode_workspace_bytes", "online_softmax_rows",
+           "online_softmax_topk_rows", "load_library", "OsfaError"]

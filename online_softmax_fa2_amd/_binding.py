@@ -1,0 +1,150 @@
+"""ctypes binding over libosfa.so: argument marshalling only.
+
+Every computation happens in the HIP kernels behind the C ABI
+(``include/osfa.h``).  PyTorch supplies device memory and the current stream.
+If the library is not built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libosfa.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP"}
+
+_lib = None
+
+
+class OsfaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libosfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m online_softmax_fa2_amd.build` "
+                           "(or __graft_entry__.build()) first; there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [i, p, p, p, p, p, i, i, i, i, f, i, i, p, p]
+    lib.attn_fwd.restype = i
+    lib.attn_decode_splitkv_workspace_bytes.argtypes = [i, i, i, i]
+    lib.attn_decode_splitkv_workspace_bytes.restype = sz
+    lib.attn_decode_splitkv.argtypes = [i, p, p, p, p, i, i, i, i, i, p, sz, p]
+    lib.attn_decode_splitkv.restype = i
+    lib.online_softmax_rows.argtypes = [p, p, i, i, p]
+    lib.online_softmax_rows.restype = i
+    lib.online_softmax_topk_rows.argtypes = [p, p, p, p, i, i, i, p]
+    lib.online_softmax_topk_rows.restype = i
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.osfa_version.argtypes = []
+    lib.osfa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        raise OsfaError(status, load_library().attn_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need_device(*ts) -> None:
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+_DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0,
+             kv_len=None, out=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v) for [B, H, N, d] tensors (f32 or bf16)."""
+    _need_device(q, k, v, kv_len, out, lse)
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B):
+        raise ValueError("kv_len must be int32 [B]")
+    _check(load_library().attn_fwd(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                   float(scale), int(bool(causal)), int(window), _ptr(kv_len), _stream(stream)))
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, H: int, d: int, nsplit: int) -> int:
+    return int(load_library().attn_decode_splitkv_workspace_bytes(B, H, d, nsplit))
+
+
+def attn_decode_splitkv(q, k, v, nsplit: int, out=None, workspace=None, stream=None):
+    """o [B, H, d] float32 from q [B, H, d] and K, V [B, H, Nkv, d]."""
+    _need_device(q, k, v, out, workspace)
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, Nkv, d = k.shape
+    if q.shape != (B, H, d) or v.shape != k.shape:
+        raise ValueError("q must be [B, H, d] and K, V [B, H, Nkv, d]")
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, d, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    _check(load_library().attn_decode_splitkv(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Nkv, d,
+                                              int(nsplit), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)))
+    return out
+
+
+def online_softmax_rows(x, out=None, stream=None):
+    """y = softmax(x, dim=-1) for a 2-D float32 tensor."""
+    _need_device(x, out)
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be a 2-D float32 tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    rows, cols = x.shape
+    _check(load_library().online_softmax_rows(_ptr(x), _ptr(out), rows, cols, _stream(stream)))
+    return out
+
+
+def online_softmax_topk_rows(x, k: int, with_probs: bool = False, stream=None):
+    """(topv [rows, k] float32, topi [rows, k] int32[, y]) of softmax(x) per row."""
+    _need_device(x)
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be a 2-D float32 tensor")
+    rows, cols = x.shape
+    topv = torch.empty((rows, k), dtype=torch.float32, device=x.device)
+    topi = torch.empty((rows, k), dtype=torch.int32, device=x.device)
+    y = torch.empty_like(x) if with_probs else None
+    _check(load_library().online_softmax_topk_rows(_ptr(x), _ptr(y), _ptr(topv), _ptr(topi), rows, cols, int(k),
+                                                   _stream(stream)))
+    return (topv, topi, y) if with_probs else (topv, topi)

@@ -1,0 +1,118 @@
+// Host side of the C ABI declared in include/osfa.h: argument validation
+// (before any launch), dispatch to the kernel launchers, error reporting.
+#include "osfa.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+attn_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ATTN_OK;
+  return fail(ATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+constexpr long long kMaxElems = 1LL << 40;
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_last_error; }
+
+const char* osfa_version(void) { return "osfa 0.1.0 (gfx950)"; }
+
+attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                       int B, int H, int N, int d, float scale, int causal, int window, const int32_t* kv_len,
+                       hipStream_t stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: unknown dtype %d", (int)dtype);
+  if (!Q || !K || !V || !O || !LSE) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: null tensor pointer");
+  if (B < 1 || H < 1 || N < 1 || d < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: sizes must be >= 1 (B=%d H=%d N=%d d=%d)", B, H, N, d);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim d=%d not built (64 or 128)", d);
+  if ((long long)B * H * N * d >= kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: B*H*N*d too large");
+  if ((long long)B * H >= (1LL << 24)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: B*H too large");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: scale must be finite and > 0 (got %g)", (double)scale);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: causal must be 0 or 1");
+  if (window < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: window must be >= 0 (0 = no window)");
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: Q, K, V, O must be 16-byte aligned");
+  osfa::FwdArgs a{Q, K, V, O, LSE, kv_len, B, H, N, d, scale, causal, window};
+  const hipError_t e = dtype == ATTN_BF16 ? osfa::launch_attn_fwd_bf16(a, stream) : osfa::launch_attn_fwd_f32(a, stream);
+  return hip_status(e, "attn_fwd");
+}
+
+size_t attn_decode_splitkv_workspace_bytes(int B, int H, int d, int nsplit) {
+  if (B < 1 || H < 1 || d < 1 || nsplit < 1) return 0;
+  return (size_t)B * H * nsplit * (size_t)(d + 2) * sizeof(float);
+}
+
+attn_status_t attn_decode_splitkv(attn_dtype_t dtype, const void* q, const void* K, const void* V, float* o, int B,
+                                  int H, int Nkv, int d, int nsplit, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: unknown dtype %d", (int)dtype);
+  if (!q || !K || !V || !o || !workspace) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: null pointer");
+  if (B < 1 || H < 1 || Nkv < 1 || d < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: sizes must be >= 1 (B=%d H=%d Nkv=%d d=%d)", B, H, Nkv, d);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv: d=%d not built (64 or 128)", d);
+  if (nsplit < 1 || nsplit > Nkv || nsplit > 4096)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: nsplit=%d must be in [1, min(Nkv, 4096)]", nsplit);
+  if ((long long)B * H * Nkv * d >= kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: too large");
+  if ((long long)B * H * nsplit >= (1LL << 31)) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: grid too large");
+  const size_t need = attn_decode_splitkv_workspace_bytes(B, H, d, nsplit);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (((uintptr_t)q | (uintptr_t)K | (uintptr_t)V) & 15)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: q, K, V must be 16-byte aligned");
+  if (((uintptr_t)o | (uintptr_t)workspace) & 3)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: o and workspace must be 4-byte aligned");
+  osfa::DecodeArgs a{q, K, V, o, static_cast<float*>(workspace), B, H, Nkv, d, nsplit};
+  const hipError_t e = dtype == ATTN_BF16 ? osfa::launch_decode_bf16(a, stream) : osfa::launch_decode_f32(a, stream);
+  return hip_status(e, "attn_decode_splitkv");
+}
+
+attn_status_t online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream) {
+  if (!x || !y) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: null pointer");
+  if (rows < 1 || cols < 1) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: rows=%d cols=%d must be >= 1", rows, cols);
+  if (cols > (1 << 28)) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: cols=%d > 2^28", cols);
+  if (((uintptr_t)x | (uintptr_t)y) & 3) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: x, y must be 4-byte aligned");
+  if (x != y) {
+    const char* xb = reinterpret_cast<const char*>(x);
+    const char* yb = reinterpret_cast<const char*>(y);
+    const size_t bytes = (size_t)rows * cols * sizeof(float);
+    if (xb < yb + bytes && yb < xb + bytes)
+      return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: x and y overlap partially");
+  }
+  return hip_status(osfa::launch_softmax_rows(x, y, rows, cols, stream), "online_softmax_rows");
+}
+
+attn_status_t online_softmax_topk_rows(const float* x, float* y, float* topv, int32_t* topi, int rows, int cols, int k,
+                                       hipStream_t stream) {
+  if (!x || !topv || !topi) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: null pointer");
+  if (rows < 1 || cols < 1) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: rows=%d cols=%d must be >= 1", rows, cols);
+  if (cols > (1 << 28)) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: cols=%d > 2^28", cols);
+  if (k < 1 || k > cols) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: k=%d must be in [1, cols]", k);
+  if (k > 16) return fail(ATTN_ERR_UNSUPPORTED, "online_softmax_topk_rows: k=%d > 16 not built", k);
+  if (((uintptr_t)x | (uintptr_t)topv | (uintptr_t)topi | (uintptr_t)y) & 3)
+    return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: pointers must be 4-byte aligned");
+  if (y == x) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: y must not alias x");
+  return hip_status(osfa::launch_softmax_topk(x, y, topv, topi, rows, cols, k, stream), "online_softmax_topk_rows");
+}
+
+}  // extern "C"

@@ -1,0 +1,229 @@
+// Split-KV decode for gfx950: one query per (b, h), the keys split across
+// workgroups, each split running the online-softmax recurrence and leaving
+// a partial (m, l, a) triple, then a merge kernel combining the partials
+// with the rescale rule (page "Derive online softmax, prove it is exact",
+// the batch-1 decoding follow-up; article "Online softmax", Step 4 and the
+// Flash-Decoding note under "Trade-offs and edge cases").
+//
+// This path streams K and V once and does a few FLOPs per byte, so it is
+// HBM-bound: the design goal is full-width coalesced 16-byte loads with many
+// bytes in flight, not matrix cores.  Layout of the work:
+//   * grid = B * H * nsplit workgroups of 4 waves; split c of (b, h) covers
+//     keys [c L, min((c + 1) L, Nkv)), L = ceil(Nkv / nsplit);
+//   * a key row (d elements) is read by D/8 consecutive lanes, 8 elements
+//     (16 B for bf16) each, so one wave-wide load covers 64 / (D/8)
+//     consecutive key rows, contiguous in memory;
+//   * each lane group (the D/8 lanes of one key slot) keeps its own
+//     (m, l, a[8 d per lane]) over the keys it visits; the score of a key is
+//     the group's dot-product partials summed with DPP row operations;
+//   * at the end the 4 * 64/(D/8) group states are merged through LDS by the
+//     same rule and written as the split's partial.
+// Partials (workspace, float32): [B, H, nsplit, D + 2] = (m, l, a[0..D)),
+// with m in log2 units of the scaled score (m = log2(e) * max score).
+#include "device_common.h"
+#include "launch.h"
+
+namespace osfa {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kUnroll = 8;  // key rows per lane per step (loads in flight)
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  // 8 elements = 16 bytes
+  typedef u32x4 Vec;
+  __device__ static inline void unpack(const Vec& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(v[i]);
+      f[2 * i + 1] = bf16_hi(v[i]);
+    }
+  }
+};
+template <>
+struct Elem<float> {
+  struct Vec {
+    f32x4 a, b;
+  };
+  __device__ static inline void unpack(const Vec& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = v.a[i];
+      f[4 + i] = v.b[i];
+    }
+  }
+};
+
+// Sum over each aligned group of G lanes (G = 8 or 16) with DPP row ops:
+// xor-1 and xor-2 quad permutes, then mirror within 8, then within 16.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+  if constexpr (G == 16)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
+  return x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const T* __restrict__ q,
+                                                                     const T* __restrict__ K,
+                                                                     const T* __restrict__ V,
+                                                                     float* __restrict__ ws, int Nkv,
+                                                                     int nsplit, int L, float c) {
+  typedef typename Elem<T>::Vec Vec;
+  constexpr int G = D / 8;             // lanes per key row
+  constexpr int SLOTS = 64 / G;        // key rows per wave-wide load
+  constexpr int WAVES = kDecThreads / 64;
+  constexpr int STEP = WAVES * SLOTS * kUnroll;  // keys per workgroup step
+  constexpr int NGROUPS = WAVES * SLOTS;
+
+  const int wg = blockIdx.x;
+  const int split = wg % nsplit;
+  const int bh = wg / nsplit;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int slot = lane / G;
+  const int dc = lane % G;  // d chunk: d = 8 dc + [0, 8)
+
+  const size_t kv_off = (size_t)bh * (size_t)Nkv * D;
+  const T* Kh = K + kv_off;
+  const T* Vh = V + kv_off;
+  float qf[8];
+  Elem<T>::unpack(*reinterpret_cast<const Vec*>(q + (size_t)bh * D + 8 * dc), qf);
+
+  const int lo = split * L;
+  const int hi = min(lo + L, Nkv);
+
+  float m = kNegInf, l = 0.0f;
+  float a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = 0.0f;
+
+  for (int base = lo; base < hi; base += STEP) {
+    Vec kv[kUnroll], vv[kUnroll];
+    int jj[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = base + (u * WAVES + w) * SLOTS + slot;
+      jj[u] = j;
+      const int js = j < hi ? j : hi - 1;
+      kv[u] = *reinterpret_cast<const Vec*>(Kh + (size_t)js * D + 8 * dc);
+      vv[u] = *reinterpret_cast<const Vec*>(Vh + (size_t)js * D + 8 * dc);
+    }
+    float s[kUnroll];
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float kf[8];
+      Elem<T>::unpack(kv[u], kf);
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], kf[e], part);
+      part = group_sum<G>(part);
+      s[u] = jj[u] < hi ? part : kNegInf;
+      mx = fmaxf(mx, s[u]);
+    }
+    const float m_new = fmaxf(m, mx * c);
+    const float m_ref = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m - m_ref);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float pexp = fast_exp2(fmaf(s[u], c, -m_ref));
+      l += pexp;
+      float vf[8];
+      Elem<T>::unpack(vv[u], vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = fmaf(pexp, vf[e], a[e]);
+    }
+    m = m_new;
+  }
+
+  // Merge the NGROUPS group states of the workgroup.
+  __shared__ float sm[NGROUPS], sl[NGROUPS];
+  __shared__ float sa[NGROUPS][D];
+  const int g = w * SLOTS + slot;
+  if (dc == 0) {
+    sm[g] = m;
+    sl[g] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sa[g][8 * dc + e] = a[e];
+  __syncthreads();
+  float* out = ws + ((size_t)bh * nsplit + split) * (D + 2);
+  for (int d = tid; d < D; d += kDecThreads) {
+    float M = kNegInf;
+    for (int i = 0; i < NGROUPS; ++i) M = fmaxf(M, sm[i]);
+    float lt = 0.0f, at = 0.0f;
+    for (int i = 0; i < NGROUPS; ++i) {
+      const float wgt = (sm[i] == kNegInf) ? 0.0f : fast_exp2(sm[i] - M);
+      lt = fmaf(wgt, sl[i], lt);
+      at = fmaf(wgt, sa[i][d], at);
+    }
+    out[2 + d] = at;
+    if (d == 0) {
+      out[0] = M;
+      out[1] = lt;
+    }
+  }
+}
+
+// One workgroup per (b, h): o = sum_c w_c a_c / sum_c w_c l_c with
+// w_c = 2^(m_c - M), M = max_c m_c, and w_c = 0 for an empty split.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws, float* __restrict__ o,
+                                                         int nsplit) {
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* part = ws + (size_t)bh * nsplit * (D + 2);
+  float M = kNegInf;
+  for (int cidx = 0; cidx < nsplit; ++cidx) M = fmaxf(M, part[(size_t)cidx * (D + 2)]);
+  float lt = 0.0f, at = 0.0f;
+  for (int cidx = 0; cidx < nsplit; ++cidx) {
+    const float* pc = part + (size_t)cidx * (D + 2);
+    const float mc = pc[0];
+    const float wgt = (mc == kNegInf) ? 0.0f : fast_exp2(mc - M);
+    lt = fmaf(wgt, pc[1], lt);
+    at = fmaf(wgt, pc[2 + d], at);
+  }
+  o[(size_t)bh * D + d] = lt > 0.0f ? at / lt : 0.0f;
+}
+
+template <typename T>
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const int L = (a.Nkv + a.nsplit - 1) / a.nsplit;
+  const float c = (float)(1.0 / __builtin_sqrt((double)a.d)) * kLog2e;
+  const unsigned nwg = (unsigned)(a.B * a.H * a.nsplit);
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  if (a.d == 128) {
+    hipLaunchKernelGGL((decode_partial_kernel<T, 128>), dim3(nwg), dim3(kDecThreads), 0, stream, q, k, v, a.ws,
+                       a.Nkv, a.nsplit, L, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.B * a.H), dim3(128), 0, stream, a.ws, a.o, a.nsplit);
+  } else {
+    hipLaunchKernelGGL((decode_partial_kernel<T, 64>), dim3(nwg), dim3(kDecThreads), 0, stream, q, k, v, a.ws,
+                       a.Nkv, a.nsplit, L, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.B * a.H), dim3(64), 0, stream, a.ws, a.o, a.nsplit);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_decode<__bf16>(a, stream); }
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) { return launch_decode<float>(a, stream); }
+
+}  // namespace osfa

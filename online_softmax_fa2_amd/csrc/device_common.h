@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels: vector types, exp2, bf16
+// packing, wavefront reductions and the associative merge of (m, d) pairs.
+//
+// Conventions used by every kernel in this library:
+//   * exponentials are computed as exp2 with log2(e) folded into the score
+//     scale, so running maxima are kept in log2 units; LSE is converted back
+//     to natural-log units once per row;
+//   * a wavefront has 64 lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane (l xor 32): exchanges the two 32-lane halves of the wave.
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Butterfly all-reductions over the full 64-lane wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) x = fmaxf(x, __shfl_xor(x, s, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s, 64);
+  return x;
+}
+
+// All-reduction over each aligned group of 16 lanes.
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int s = 1; s < 16; s <<= 1) x += __shfl_xor(x, s, 64);
+  return x;
+}
+
+// Merge two online-normalizer pairs (m in log2 units): the larger maximum
+// wins and each sum is rescaled to it before adding (article "Online
+// softmax", Step 4).  (-inf, 0) is the identity.
+struct MD {
+  float m, d;
+};
+__device__ __forceinline__ MD md_merge(MD a, MD b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == kNegInf) return MD{kNegInf, 0.0f};
+  const float wa = (a.m == kNegInf) ? 0.0f : fast_exp2(a.m - M);
+  const float wb = (b.m == kNegInf) ? 0.0f : fast_exp2(b.m - M);
+  return MD{M, a.d * wa + b.d * wb};
+}
+
+__device__ __forceinline__ MD wave_md_merge(MD v) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    MD o{__shfl_xor(v.m, s, 64), __shfl_xor(v.d, s, 64)};
+    v = md_merge(v, o);
+  }
+  return v;
+}
+
+// bf16 helpers.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+}  // namespace osfa

@@ -1,0 +1,42 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel
+// translation units.  Arguments reaching a launcher have been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace osfa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_len;  // device [B] or nullptr
+  int B, H, N, d;
+  float scale;
+  int causal, window;
+};
+
+// Each returns the hipError_t of its launch(es).
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* ws;  // [B, H, nsplit, d + 2]
+  int B, H, Nkv, d, nsplit;
+};
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream);
+hipError_t launch_softmax_topk(const float* x, float* y, float* topv, int32_t* topi, int rows,
+                               int cols, int k, hipStream_t stream);
+
+}  // namespace osfa

@@ -1,0 +1,304 @@
+// Row-wise online softmax and softmax fused with top-k, float32, gfx950.
+//
+// Method (article "Online softmax"): pass 1 computes the pair (m, d), the
+// row maximum and the sum of exp(x - m), keeping a running maximum and
+// rescaling the running sum by exp(m_old - m_new) when it grows (Step 2);
+// partial pairs of lanes and waves are combined by the associative merge
+// (Step 4); pass 2 writes exp(x - m) / d (Step 3).  The fused variant keeps
+// a top-k list next to (m, d) during the single pass and outputs only the k
+// probabilities and their column indices (Step 3, fusion with top-k).
+//
+// gfx950 mapping: one 256-thread workgroup per row.  Each lane folds its
+// elements into its own (m, d) a chunk at a time (chunk maximum, one rescale
+// of d, one exp2 per element with log2(e) folded into an FMA), then the 64
+// lanes of a wave merge by butterfly exchanges and the 4 waves through LDS.
+// Rows of up to 8192 columns are held in registers between the passes, so
+// HBM sees one read and one write per element; longer rows re-read x.
+// Accesses are float4 (16 B per lane, fully coalesced) when the row length
+// is a multiple of 4 and the pointers are 16-byte aligned, else scalar.
+#include "device_common.h"
+#include "launch.h"
+
+namespace osfa {
+namespace {
+
+constexpr int kSmThreads = 256;
+constexpr int kSmWaves = kSmThreads / 64;
+
+template <int W>
+__device__ __forceinline__ void ld(const float* p, float* v) {
+  if constexpr (W == 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+    v[0] = t[0];
+    v[1] = t[1];
+    v[2] = t[2];
+    v[3] = t[3];
+  } else {
+    v[0] = *p;
+  }
+}
+template <int W>
+__device__ __forceinline__ void st(float* p, const float* v) {
+  if constexpr (W == 4) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    *p = v[0];
+  }
+}
+
+// Fold a chunk of n values (maximum mx, raw units) into the running pair.
+__device__ __forceinline__ void fold_chunk(MD& r, float mx, const float* vals, int n) {
+  const float m_new = fmaxf(r.m, mx * kLog2e);
+  const float m_ref = (m_new == kNegInf) ? 0.0f : m_new;
+  float s = r.d * fast_exp2(r.m - m_ref);
+  for (int i = 0; i < n; ++i) s += fast_exp2(fmaf(vals[i], kLog2e, -m_ref));
+  r.m = m_new;
+  r.d = s;
+}
+
+// Merge the pairs of all lanes of the workgroup; every thread gets the result.
+__device__ __forceinline__ MD block_md(MD v) {
+  __shared__ MD sh[kSmWaves];
+  v = wave_md_merge(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  MD r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kSmWaves; ++i) r = md_merge(r, sh[i]);
+  return r;
+}
+
+// Register-resident rows: thread t owns accesses t + 256 i, i < VPT.
+template <int W, int VPT>
+__global__ __launch_bounds__(kSmThreads) void softmax_rows_reg_kernel(const float* x, float* y, int cols) {
+  const int row = blockIdx.x;
+  const float* xr = x + (size_t)row * cols;
+  float* yr = y + (size_t)row * cols;
+  const int nacc = cols / W;
+  const int t = threadIdx.x;
+  float v[VPT][W];
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int a = t + kSmThreads * i;
+    if (a < nacc) {
+      ld<W>(xr + (size_t)a * W, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < W; ++e) v[i][e] = kNegInf;
+    }
+#pragma unroll
+    for (int e = 0; e < W; ++e) mx = fmaxf(mx, v[i][e]);
+  }
+  MD r{kNegInf, 0.0f};
+  fold_chunk(r, mx, &v[0][0], VPT * W);  // -inf slots contribute exp2(-inf) = 0
+  r = block_md(r);
+  const float inv = 1.0f / r.d;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int a = t + kSmThreads * i;
+    if (a < nacc) {
+      float o[W];
+#pragma unroll
+      for (int e = 0; e < W; ++e) o[e] = fast_exp2(fmaf(v[i][e], kLog2e, -r.m)) * inv;
+      st<W>(yr + (size_t)a * W, o);
+    }
+  }
+}
+
+// Any row length: pass 1 streams x into the pair, pass 2 re-reads x.
+template <int W>
+__device__ __forceinline__ MD stream_md(const float* xr, int nacc) {
+  constexpr int U = 4;
+  MD r{kNegInf, 0.0f};
+  for (int base = 0; base < nacc; base += kSmThreads * U) {
+    float v[U][W];
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int a = base + threadIdx.x + kSmThreads * u;
+      if (a < nacc) {
+        ld<W>(xr + (size_t)a * W, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < W; ++e) v[u][e] = kNegInf;
+      }
+#pragma unroll
+      for (int e = 0; e < W; ++e) mx = fmaxf(mx, v[u][e]);
+    }
+    fold_chunk(r, mx, &v[0][0], U * W);
+  }
+  return r;
+}
+
+template <int W>
+__device__ __forceinline__ void stream_write(const float* xr, float* yr, int nacc, MD r) {
+  const float inv = 1.0f / r.d;
+  for (int a = threadIdx.x; a < nacc; a += kSmThreads) {
+    float v[W];
+    ld<W>(xr + (size_t)a * W, v);
+#pragma unroll
+    for (int e = 0; e < W; ++e) v[e] = fast_exp2(fmaf(v[e], kLog2e, -r.m)) * inv;
+    st<W>(yr + (size_t)a * W, v);
+  }
+}
+
+template <int W>
+__global__ __launch_bounds__(kSmThreads) void softmax_rows_stream_kernel(const float* x, float* y, int cols) {
+  const int row = blockIdx.x;
+  const float* xr = x + (size_t)row * cols;
+  float* yr = y + (size_t)row * cols;
+  const int nacc = cols / W;
+  MD r = block_md(stream_md<W>(xr, nacc));
+  stream_write<W>(xr, yr, nacc, r);
+}
+
+// ---------------------------------------------------------------------------
+// Softmax fused with top-k.
+//
+// Each wave keeps its current top-k candidates in lanes 0..k-1 (lane i holds
+// the i-th best, order: larger x first, lower column index on equal x) and
+// a wave-uniform threshold T = x of the k-th entry.  Elements below T cannot
+// enter the list, so after the first few steps almost every step is a single
+// compare and ballot; the rare candidates are inserted one at a time with a
+// one-lane shift of the list.  At the end the 4 waves' lists are ranked in
+// LDS and the k best are written with their probabilities exp(x - m) / d.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bool better(float xa, int ia, float xb, int ib) {
+  return xa > xb || (xa == xb && ia < ib);
+}
+
+template <int W>
+__global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x, float* y, float* topv,
+                                                                   int32_t* topi, int cols, int k) {
+  constexpr int U = 4;
+  const int row = blockIdx.x;
+  const float* xr = x + (size_t)row * cols;
+  const int nacc = cols / W;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+
+  float lx = kNegInf;  // this lane's list entry (lanes < k)
+  int li = 0x7fffffff;
+  float T = kNegInf;  // wave-uniform: x of the k-th entry
+  MD r{kNegInf, 0.0f};
+
+  for (int base = 0; base < nacc; base += kSmThreads * U) {
+    float v[U][W];
+    float mx = kNegInf;
+    bool cand = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int a = base + threadIdx.x + kSmThreads * u;
+      if (a < nacc) {
+        ld<W>(xr + (size_t)a * W, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < W; ++e) v[u][e] = kNegInf;
+      }
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        mx = fmaxf(mx, v[u][e]);
+        cand = cand || (a < nacc && v[u][e] >= T);
+      }
+    }
+    fold_chunk(r, mx, &v[0][0], U * W);
+
+    uint64_t mask = __ballot(cand);
+    while (mask) {
+      const int src = __builtin_ctzll(mask);
+      mask &= mask - 1;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int a_src = base + (w * 64 + src) + kSmThreads * u;
+        if (a_src >= nacc) continue;
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+          const float cx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[u][e]), src));
+          const int ci = a_src * W + e;
+          if (!(cx >= T)) continue;  // wave-uniform
+          const bool mine = lane < k && better(cx, ci, lx, li);
+          const float px = __shfl_up(lx, 1, 64);
+          const int pi = __shfl_up(li, 1, 64);
+          const bool prev_better = lane > 0 && better(px, pi, cx, ci);
+          if (mine) {
+            if (lane == 0 || prev_better) {
+              lx = cx;
+              li = ci;
+            } else {
+              lx = px;
+              li = pi;
+            }
+          }
+          T = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), k - 1));
+        }
+      }
+    }
+  }
+
+  r = block_md(r);  // contains a __syncthreads
+
+  __shared__ float cx_s[kSmWaves * 16];
+  __shared__ int ci_s[kSmWaves * 16];
+  if (lane < k) {
+    cx_s[w * k + lane] = lx;
+    ci_s[w * k + lane] = li;
+  }
+  __syncthreads();
+  if (w == 0 && lane < kSmWaves * k) {
+    const float mx = cx_s[lane];
+    const int mi = ci_s[lane];
+    int rank = 0;
+    for (int j = 0; j < kSmWaves * k; ++j) rank += better(cx_s[j], ci_s[j], mx, mi) ? 1 : 0;
+    if (rank < k) {
+      topv[(size_t)row * k + rank] = fast_exp2(fmaf(mx, kLog2e, -r.m)) / r.d;
+      topi[(size_t)row * k + rank] = mi;
+    }
+  }
+  if (y) stream_write<W>(xr, y + (size_t)row * cols, nacc, r);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+hipError_t launch_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream) {
+  const bool vec = (cols % 4 == 0) && aligned16(x) && aligned16(y);
+  const dim3 grid(rows), block(kSmThreads);
+  if (vec) {
+    const int nacc = cols / 4;
+    if (nacc <= 256)
+      hipLaunchKernelGGL((softmax_rows_reg_kernel<4, 1>), grid, block, 0, stream, x, y, cols);
+    else if (nacc <= 512)
+      hipLaunchKernelGGL((softmax_rows_reg_kernel<4, 2>), grid, block, 0, stream, x, y, cols);
+    else if (nacc <= 1024)
+      hipLaunchKernelGGL((softmax_rows_reg_kernel<4, 4>), grid, block, 0, stream, x, y, cols);
+    else if (nacc <= 2048)
+      hipLaunchKernelGGL((softmax_rows_reg_kernel<4, 8>), grid, block, 0, stream, x, y, cols);
+    else
+      hipLaunchKernelGGL((softmax_rows_stream_kernel<4>), grid, block, 0, stream, x, y, cols);
+  } else {
+    if (cols <= 1024)
+      hipLaunchKernelGGL((softmax_rows_reg_kernel<1, 4>), grid, block, 0, stream, x, y, cols);
+    else if (cols <= 4096)
+      hipLaunchKernelGGL((softmax_rows_reg_kernel<1, 16>), grid, block, 0, stream, x, y, cols);
+    else
+      hipLaunchKernelGGL((softmax_rows_stream_kernel<1>), grid, block, 0, stream, x, y, cols);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_topk(const float* x, float* y, float* topv, int32_t* topi, int rows, int cols, int k,
+                               hipStream_t stream) {
+  const bool vec = (cols % 4 == 0) && aligned16(x) && (y == nullptr || aligned16(y));
+  const dim3 grid(rows), block(kSmThreads);
+  if (vec)
+    hipLaunchKernelGGL((softmax_topk_kernel<4>), grid, block, 0, stream, x, y, topv, topi, cols, k);
+  else
+    hipLaunchKernelGGL((softmax_topk_kernel<1>), grid, block, 0, stream, x, y, topv, topi, cols, k);
+  return hipGetLastError();
+}
+
+}  // namespace osfa

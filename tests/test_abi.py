@@ -1,0 +1,164 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+and rejects invalid arguments on the host before any launch.
+
+No call here reaches a kernel launch: every call fails validation first
+(the fake pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from online_softmax_fa2_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "osfa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from online_softmax_fa2_amd.build import build_library
+        build_library()
+    return bd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("attn_fwd", "attn_decode_splitkv", "attn_decode_splitkv_workspace_bytes",
+                 "online_softmax_rows", "online_softmax_topk_rows", "attn_last_error", "osfa_version"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in osfa.h but not exported"
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.osfa_version()
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced
+
+
+def _fwd(lib, **kw):
+    a = dict(dtype=bd.ATTN_BF16, Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, B=1, H=1, N=16, d=128, scale=0.1,
+             causal=0, window=0, kv_len=None, stream=None)
+    a.update(kw)
+    return lib.attn_fwd(a["dtype"], a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["d"],
+                        a["scale"], a["causal"], a["window"], a["kv_len"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Q=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(LSE=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(N=0), bd.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(B=-1), bd.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(d=96), bd.ATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(d=256), bd.ATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(scale=0.0), bd.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=-1.0), bd.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), bd.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("inf")), bd.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(causal=2), bd.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(window=-3), bd.ATTN_ERR_INVALID_ARG, "window"),
+    (dict(dtype=7), bd.ATTN_ERR_INVALID_ARG, "dtype"),
+    (dict(Q=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(B=1 << 12, H=1 << 12, N=1 << 12, d=128), bd.ATTN_ERR_INVALID_ARG, "too large"),
+])
+def test_attn_fwd_rejects(lib, kw, status, msg):
+    assert _fwd(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_workspace_bytes(lib):
+    assert lib.attn_decode_splitkv_workspace_bytes(1, 32, 128, 64) == 32 * 64 * 130 * 4
+    assert lib.attn_decode_splitkv_workspace_bytes(2, 3, 64, 7) == 2 * 3 * 7 * 66 * 4
+    assert lib.attn_decode_splitkv_workspace_bytes(0, 3, 64, 7) == 0
+    assert lib.attn_decode_splitkv_workspace_bytes(1, 3, 64, 0) == 0
+
+
+def _dec(lib, **kw):
+    a = dict(dtype=bd.ATTN_BF16, q=FAKE, K=FAKE, V=FAKE, o=FAKE, B=1, H=2, Nkv=100, d=128, nsplit=4, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.attn_decode_splitkv(a["dtype"], a["q"], a["K"], a["V"], a["o"], a["B"], a["H"], a["Nkv"], a["d"],
+                                   a["nsplit"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(ws=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(Nkv=0), bd.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(d=80), bd.ATTN_ERR_UNSUPPORTED, "not built"),
+    (dict(nsplit=0), bd.ATTN_ERR_INVALID_ARG, "nsplit"),
+    (dict(nsplit=101), bd.ATTN_ERR_INVALID_ARG, "nsplit"),
+    (dict(Nkv=100000, nsplit=5000), bd.ATTN_ERR_INVALID_ARG, "nsplit"),
+    (dict(ws_bytes=2 * 4 * 130 * 4 - 1), bd.ATTN_ERR_INVALID_ARG, "workspace"),
+    (dict(K=FAKE + 4), bd.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(dtype=3), bd.ATTN_ERR_INVALID_ARG, "dtype"),
+])
+def test_decode_rejects(lib, kw, status, msg):
+    assert _dec(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((None, FAKE, 4, 4), "null"),
+    ((FAKE, FAKE, 0, 4), "rows"),
+    ((FAKE, FAKE, 4, 0), "rows"),
+    ((FAKE, FAKE + 4 * 3, 4, 4), "overlap"),
+    ((FAKE + 1, FAKE + 1, 4, 4), "aligned"),
+])
+def test_softmax_rejects(lib, args, msg):
+    x, y, rows, cols = args
+    assert lib.online_softmax_rows(x, y, rows, cols, None) == bd.ATTN_ERR_INVALID_ARG
+    assert msg in lib.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(k=0), bd.ATTN_ERR_INVALID_ARG, "k=0"),
+    (dict(k=11, cols=10), bd.ATTN_ERR_INVALID_ARG, "k=11"),
+    (dict(k=17), bd.ATTN_ERR_UNSUPPORTED, "k=17"),
+    (dict(x=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(topi=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(y=FAKE), bd.ATTN_ERR_INVALID_ARG, "alias"),
+    (dict(rows=0), bd.ATTN_ERR_INVALID_ARG, "rows"),
+])
+def test_topk_rejects(lib, kw, status, msg):
+    a = dict(x=FAKE, y=None, topv=FAKE * 2, topi=FAKE * 3, rows=4, cols=100, k=5)
+    a.update(kw)
+    assert lib.online_softmax_topk_rows(a["x"], a["y"], a["topv"], a["topi"], a["rows"], a["cols"], a["k"],
+                                        None) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_error_text_is_per_thread(lib):
+    import threading
+    assert _fwd(lib, d=96) == bd.ATTN_ERR_UNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["text"] = lib.attn_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["text"] == ""
+    assert "head dim" in lib.attn_last_error().decode()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        bd.online_softmax_rows(x)

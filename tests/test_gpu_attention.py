@@ -1,0 +1,151 @@
+"""GPU parity: attn_fwd (float32 and bfloat16) against the FP64 oracle.
+
+Small cases span several 128-query tiles and 64-key blocks with ragged
+tails, every mask combination, fully masked rows and late maxima; the full
+workloads are checked on whole heads plus rows sampled across all heads,
+in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_fa2_amd as osfa
+from online_softmax_fa2_amd.inputs import WORKLOADS, attn_inputs, workload_attn_inputs
+from oracle import attention_ref
+from tests.gpu_util import (Guarded, assert_bf16_out, assert_f32_rel, assert_lse_abs, assert_normwise, upload_bf16,
+                            upload_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(inp):
+    if inp.dtype == "bf16":
+        q, k, v = upload_bf16(inp.q_bits), upload_bf16(inp.k_bits), upload_bf16(inp.v_bits)
+        odt = torch.bfloat16
+    else:
+        q, k, v = upload_f32(inp.q), upload_f32(inp.k), upload_f32(inp.v)
+        odt = torch.float32
+    B, H, N, d = inp.q.shape
+    o = Guarded((B, H, N, d), odt)
+    lse = Guarded((B, H, N), torch.float32)
+    kvl = None if inp.kv_len is None else torch.from_numpy(inp.kv_len).to("cuda:0")
+    osfa.attn_fwd(q, k, v, scale=inp.scale, causal=inp.causal, window=inp.window, kv_len=kvl, out=o.t, lse=lse.t)
+    torch.cuda.synchronize()
+    o.check()
+    lse.check()
+    return o.t.float().cpu().numpy(), lse.t.cpu().numpy()
+
+
+def check(inp, O, L, rows=None, heads=None):
+    """Compare (selected heads / rows of) the GPU result with the oracle."""
+    B, H, N, d = inp.q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        Or, Lr = attention_ref(inp.q[sl], inp.k[sl], inp.v[sl], inp.scale, causal=inp.causal, window=inp.window,
+                               kv_len=None if inp.kv_len is None else inp.kv_len[b:b + 1], rows=rows)
+        og = O[b, h] if rows is None else O[b, h, rows]
+        lg = L[b, h] if rows is None else L[b, h, rows]
+        what = f"b={b} h={h}"
+        if inp.dtype == "f32":
+            assert_normwise(og, Or[0, 0], 1e-5, what=what + " O")
+            assert_f32_rel(lg, Lr[0, 0], 1e-5, what=what + " LSE", floor=1.0)
+        else:
+            assert_bf16_out(og, Or[0, 0], what=what + " O")
+            assert_lse_abs(lg, Lr[0, 0], 1e-3, what=what + " LSE")
+
+
+CASES = [
+    # (B, H, N, d, causal, window, kv_len, n_big)
+    (1, 1, 1, 64, False, 0, None, 0),
+    (1, 2, 1, 128, True, 0, None, 0),
+    (1, 2, 65, 64, False, 0, None, 0),
+    (2, 1, 129, 128, True, 0, None, 0),
+    (1, 2, 1000, 64, False, 0, None, 0),
+    (1, 2, 1000, 128, True, 0, None, 0),
+    (2, 2, 300, 64, True, 7, None, 0),
+    (1, 2, 700, 128, True, 100, [650], 3),
+    (2, 1, 500, 128, False, 60, [430, 500], 0),
+    (2, 1, 333, 64, True, 0, [0, 200], 0),        # batch 0: every row fully masked
+    (1, 1, 400, 128, True, 1, None, 0),           # each row sees only itself
+    (1, 1, 256, 64, True, 64, [100], 0),          # window + padding: rows 163.. see nothing
+    (1, 3, 513, 128, False, 0, [257], 4),
+    (3, 2, 127, 128, False, 1000, None, 0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_fwd_parity(dtype, case):
+    B, H, N, d, causal, window, kv_len, nbig = case
+    print(f"attn_fwd {dtype} B={B} H={H} N={N} d={d} causal={causal} window={window} kv_len={kv_len}", flush=True)
+    inp = attn_inputs(B, H, N, d, dtype=dtype, seed=N + d + B, causal=causal, window=window, kv_len=kv_len,
+                      n_big_keys=nbig)
+    O, L = run_fwd(inp)
+    check(inp, O, L)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd_late_maxima_and_far_apart_rows(dtype):
+    """Large scores planted in the last keys; rows whose scores sit +-1000 apart in one tile."""
+    inp = attn_inputs(1, 1, 1000, 64, dtype=dtype, seed=90)
+    inp.k[:, :, -5:, :] *= 8.0
+    if dtype == "bf16":
+        from online_softmax_fa2_amd.inputs import bf16_round
+        inp.k_bits, inp.k = bf16_round(inp.k)
+    O, L = run_fwd(inp)
+    check(inp, O, L)
+    inp2 = attn_inputs(1, 1, 256, 64, dtype=dtype, seed=91)
+    inp2.q[0, 0, ::2] *= 0.0
+    inp2.q[0, 0, ::2, 0] = 400.0
+    inp2.q[0, 0, 1::2, 0] = -400.0
+    inp2.k[0, 0, :, 0] = np.abs(inp2.k[0, 0, :, 0]) + 0.5
+    if dtype == "bf16":
+        from online_softmax_fa2_amd.inputs import bf16_round
+        inp2.q_bits, inp2.q = bf16_round(inp2.q)
+        inp2.k_bits, inp2.k = bf16_round(inp2.k)
+    O, L = run_fwd(inp2)
+    check(inp2, O, L)
+
+
+def test_fwd_closed_forms_bf16():
+    """Causal window 1: O_i = v_i exactly; V = 1: O = 1 exactly."""
+    inp = attn_inputs(1, 2, 300, 128, dtype="bf16", seed=92, causal=True, window=1)
+    O, L = run_fwd(inp)
+    assert np.array_equal(O, inp.v)
+    inp.v[:] = 1.0
+    inp.v_bits[:] = 0x3F80
+    inp.window = 0
+    O, _ = run_fwd(inp)
+    assert np.all(O == 1.0)
+
+
+def _full(name, heads, nrows=64):
+    w = WORKLOADS[name]
+    print(f"attn_fwd full workload {name}", flush=True)
+    inp = workload_attn_inputs(name)
+    O, L = run_fwd(inp)
+    assert not np.isnan(O).any() and not np.isnan(L).any()
+    check(inp, O, L, heads=heads)
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(w["N"], nrows, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, w["N"] - 1]]))
+    all_heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
+    check(inp, O, L, rows=rows, heads=all_heads[::5])
+    return inp, O, L
+
+
+def test_fwd_full_f32_n1000():
+    inp = workload_attn_inputs("attn_f32_b1h1_n1000_d64")
+    O, L = run_fwd(inp)
+    check(inp, O, L)
+
+
+def test_fwd_full_bf16_causal_2048():
+    _full("attn_bf16_causal_b4h32_n2048_d128", heads=[(0, 0), (1, 7), (3, 31)])
+
+
+def test_fwd_full_bf16_window_pad_8192():
+    inp, O, L = _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0), (0, 63)], nrows=48)
+    # every query sees at least itself or the keys before the padding: no -inf rows here
+    assert np.all(np.isfinite(L))
