@@ -178,23 +178,57 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const T* __
 
 // One workgroup per (b, h): o = sum_c w_c a_c / sum_c w_c l_c with
 // w_c = 2^(m_c - M), M = max_c m_c, and w_c = 0 for an empty split.
+// Threads first read all (m_c, l_c) in parallel and reduce M and the
+// weighted l through LDS; then thread (d, g) sums the splits c = g mod G for
+// column d, and the G partial sums are combined through LDS.
+constexpr int kMergeThreads = 256;
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws, float* __restrict__ o,
-                                                         int nsplit) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ ws,
+                                                                     float* __restrict__ o, int nsplit) {
+  constexpr int G = kMergeThreads / D;  // split groups
+  __shared__ float s_w[4096];           // nsplit <= 4096
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float s_acc[G][D];
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const float* part = ws + (size_t)bh * nsplit * (D + 2);
-  float M = kNegInf;
-  for (int cidx = 0; cidx < nsplit; ++cidx) M = fmaxf(M, part[(size_t)cidx * (D + 2)]);
-  float lt = 0.0f, at = 0.0f;
-  for (int cidx = 0; cidx < nsplit; ++cidx) {
-    const float* pc = part + (size_t)cidx * (D + 2);
-    const float mc = pc[0];
+
+  float mloc = kNegInf;
+  for (int c = tid; c < nsplit; c += kMergeThreads) mloc = fmaxf(mloc, part[(size_t)c * (D + 2)]);
+  mloc = wave_max(mloc);
+  if (lane == 0) s_red[w] = mloc;
+  __syncthreads();
+  float M = s_red[0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, s_red[i]);
+  __syncthreads();  // s_red is reused below
+
+  float lloc = 0.0f;
+  for (int c = tid; c < nsplit; c += kMergeThreads) {
+    const float mc = part[(size_t)c * (D + 2)];
     const float wgt = (mc == kNegInf) ? 0.0f : fast_exp2(mc - M);
-    lt = fmaf(wgt, pc[1], lt);
-    at = fmaf(wgt, pc[2 + d], at);
+    s_w[c] = wgt;
+    lloc = fmaf(wgt, part[(size_t)c * (D + 2) + 1], lloc);
   }
-  o[(size_t)bh * D + d] = lt > 0.0f ? at / lt : 0.0f;
+  lloc = wave_sum(lloc);
+  if (lane == 0) s_red[w] = lloc;
+  __syncthreads();
+  float lt = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMergeThreads / 64; ++i) lt += s_red[i];
+
+  const int d = tid % D, g = tid / D;
+  float at = 0.0f;
+  for (int c = g; c < nsplit; c += G) at = fmaf(s_w[c], part[(size_t)c * (D + 2) + 2 + d], at);
+  s_acc[g][d] = at;
+  __syncthreads();
+  if (g == 0) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) a += s_acc[i][d];
+    o[(size_t)bh * D + d] = lt > 0.0f ? a / lt : 0.0f;
+  }
 }
 
 template <typename T>
@@ -210,13 +244,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                        a.Nkv, a.nsplit, L, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.B * a.H), dim3(128), 0, stream, a.ws, a.o, a.nsplit);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.B * a.H), dim3(kMergeThreads), 0, stream, a.ws, a.o, a.nsplit);
   } else {
     hipLaunchKernelGGL((decode_partial_kernel<T, 64>), dim3(nwg), dim3(kDecThreads), 0, stream, q, k, v, a.ws,
                        a.Nkv, a.nsplit, L, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.B * a.H), dim3(64), 0, stream, a.ws, a.o, a.nsplit);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.B * a.H), dim3(kMergeThreads), 0, stream, a.ws, a.o, a.nsplit);
   }
   return hipGetLastError();
 }

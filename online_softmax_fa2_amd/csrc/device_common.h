@@ -28,8 +28,59 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value held by lane (l xor 32): exchanges the two 32-lane halves of the wave.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Exchange across the two 32-lane halves with v_permlane32_swap.  With
+// operands (a, b) both holding x, the instruction leaves lane l < 32 with
+// (x[l], x[l + 32]) and lane l >= 32 with (x[l - 32], x[l]).  The compiler
+// folds the two results together when both operands are the same value, so
+// the second operand is an identity DPP copy it cannot see through.
+struct HalfPair {
+  float lo, hi;  // (a, b) after the swap
+};
+__device__ __forceinline__ HalfPair permlane32_pair(float x) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, x);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xE4, 0xF, 0xF, true);  // quad_perm identity
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return HalfPair{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+// Value held by lane (l xor 32).
+__device__ __forceinline__ float swap_halves(float x) {
+  const HalfPair p = permlane32_pair(x);
+  return (__lane_id() < 32) ? p.hi : p.lo;
+}
+// max / sum of x over lanes l and l xor 32 (order-independent, no lane test).
+__device__ __forceinline__ float max_halves(float x) {
+  const HalfPair p = permlane32_pair(x);
+  return fmaxf(p.lo, p.hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const HalfPair p = permlane32_pair(x);
+  return p.lo + p.hi;
+}
+
+// DPP helpers (gfx9 encodings): row_shr:n = 0x110 + n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143.  Lanes whose source is outside the row keep `old`.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, x),
+                                                               CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Maximum over the 64 lanes, returned to every lane (an inclusive DPP scan
+// that leaves the total in lane 63, then a broadcast of lane 63).
+__device__ __forceinline__ float wave_max_bcast(float x) {
+  const float ninf = -__builtin_huge_valf();
+  x = fmaxf(x, dpp_f<0x111>(ninf, x));
+  x = fmaxf(x, dpp_f<0x112>(ninf, x));
+  x = fmaxf(x, dpp_f<0x114>(ninf, x));
+  x = fmaxf(x, dpp_f<0x118>(ninf, x));
+  x = fmaxf(x, dpp_f<0x142, 0xA>(ninf, x));
+  x = fmaxf(x, dpp_f<0x143, 0xC>(ninf, x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
 
 // Butterfly all-reductions over the full 64-lane wave.
 __device__ __forceinline__ float wave_max(float x) {

@@ -158,12 +158,16 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_stream_kernel(const f
 // Softmax fused with top-k.
 //
 // Each wave keeps its current top-k candidates in lanes 0..k-1 (lane i holds
-// the i-th best, order: larger x first, lower column index on equal x) and
-// a wave-uniform threshold T = x of the k-th entry.  Elements below T cannot
-// enter the list, so after the first few steps almost every step is a single
-// compare and ballot; the rare candidates are inserted one at a time with a
-// one-lane shift of the list.  At the end the 4 waves' lists are ranked in
-// LDS and the k best are written with their probabilities exp(x - m) / d.
+// the i-th best; order: larger x first, lower column index on equal x) and a
+// wave-uniform threshold (Tx, Ti): an element can only enter the list if it
+// beats the threshold.  The threshold starts as the k-th largest of the 64
+// lanes' maxima over the wave's first chunk (a lower bound of the wave's
+// final k-th value: those k lane maxima are k distinct elements), so even
+// the first chunk offers only a handful of candidates; later it is the
+// list's k-th entry.  Candidates are inserted one at a time (readlane to
+// broadcast, a one-lane DPP shift of the list).  At the end the 4 waves'
+// lists are ranked in LDS and the k best are written with their
+// probabilities exp(x - m) / d.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ bool better(float xa, int ia, float xb, int ib) {
@@ -182,13 +186,13 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
 
   float lx = kNegInf;  // this lane's list entry (lanes < k)
   int li = 0x7fffffff;
-  float T = kNegInf;  // wave-uniform: x of the k-th entry
+  float Tx = kNegInf;  // wave-uniform threshold
+  int Ti = 0x7fffffff;
   MD r{kNegInf, 0.0f};
 
   for (int base = 0; base < nacc; base += kSmThreads * U) {
     float v[U][W];
     float mx = kNegInf;
-    bool cand = false;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int a = base + threadIdx.x + kSmThreads * u;
@@ -199,12 +203,33 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
         for (int e = 0; e < W; ++e) v[u][e] = kNegInf;
       }
 #pragma unroll
-      for (int e = 0; e < W; ++e) {
-        mx = fmaxf(mx, v[u][e]);
-        cand = cand || (a < nacc && v[u][e] >= T);
-      }
+      for (int e = 0; e < W; ++e) mx = fmaxf(mx, v[u][e]);
     }
     fold_chunk(r, mx, &v[0][0], U * W);
+
+    if (base == 0) {
+      // Threshold from the first chunk: the k-th largest lane maximum
+      // (groups of equal maxima are counted together).
+      float lm = mx;
+      int cnt = 0;
+      while (true) {
+        const float M = wave_max_bcast(lm);
+        if (M == kNegInf) break;  // fewer than k elements in this chunk
+        const uint64_t eq = __ballot(lm == M);
+        cnt += __builtin_popcountll(eq);
+        lm = (lm == M) ? kNegInf : lm;
+        if (cnt >= k) {
+          Tx = M;
+          break;
+        }
+      }
+    }
+
+    bool cand = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < W; ++e) cand = cand || (v[u][e] >= Tx && v[u][e] != kNegInf);
 
     uint64_t mask = __ballot(cand);
     while (mask) {
@@ -213,17 +238,19 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int a_src = base + (w * 64 + src) + kSmThreads * u;
-        if (a_src >= nacc) continue;
+        if (a_src >= nacc) continue;  // wave-uniform
 #pragma unroll
         for (int e = 0; e < W; ++e) {
           const float cx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[u][e]), src));
           const int ci = a_src * W + e;
-          if (!(cx >= T)) continue;  // wave-uniform
-          const bool mine = lane < k && better(cx, ci, lx, li);
-          const float px = __shfl_up(lx, 1, 64);
-          const int pi = __shfl_up(li, 1, 64);
+          if (!better(cx, ci, Tx, Ti) && !(cx == Tx && Ti == 0x7fffffff)) continue;  // wave-uniform
+          // Insert: lanes whose entry is worse than the candidate take the
+          // previous lane's entry, or the candidate if the previous is better.
+          const bool mine = better(cx, ci, lx, li);
+          const float px = dpp_f<0x111>(kNegInf, lx);  // lane i - 1 (row 0 holds the list)
+          const int pi = dpp_i<0x111>(0x7fffffff, li);
           const bool prev_better = lane > 0 && better(px, pi, cx, ci);
-          if (mine) {
+          if (mine && lane < 16) {
             if (lane == 0 || prev_better) {
               lx = cx;
               li = ci;
@@ -232,7 +259,12 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
               li = pi;
             }
           }
-          T = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), k - 1));
+          const float kx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), k - 1));
+          const int ki = __builtin_amdgcn_readlane(li, k - 1);
+          if (better(kx, ki, Tx, Ti) || (kx == Tx && Ti == 0x7fffffff && ki != 0x7fffffff)) {
+            Tx = kx;
+            Ti = ki;
+          }
         }
       }
     }
