@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle sample budget")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three 1 GiB device-to-device copies (the reference kernel that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     return ap.parse_args()
 
 
@@ -47,6 +50,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": x.numel() * 4, "copies": 3}))
+        return
 
     import online_softmax_fa2_amd as osfa
     from online_softmax_fa2_amd import accounting as acc
@@ -154,6 +166,14 @@ def main():
 
     cpu = cpu_baseline(fin, fw, args.cpu_seconds)
 
+    # Measured HBM bytes per launch (rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE,
+    # scaled by a 1 GiB copy), recorded under profiles/ together with a hash
+    # of the kernel sources: reported only while the kernel is unchanged.
+    from online_softmax_fa2_amd.rocprof_summary import lookup
+    traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    fwd_traffic = lookup("fwd_bf16_d128_kernel", traffic_file)
+    dec_traffic = lookup("decode_partial_kernel", traffic_file)
+
     out = {
         "metric": "attn fwd TFLOP/s & %MFMA peak (N=8K,d=128 bf16); split-KV decode HBM GB/s",
         "value": round(fwd_tflops, 2),
@@ -171,8 +191,9 @@ def main():
                    "window": fw["window"], "kv_len": int(fin.kv_len[0]), "big_keys_x8": fw["n_big_keys"],
                    "algorithmic_flop": fw_flops, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": acc.PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / acc.PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_bf16_kernel<128>", "avg_launch_us": round(ms["attn_fwd"] * 1e3, 2)},
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / acc.PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if fwd_traffic is None else round(fwd_traffic),
+                     "kernel": "fwd_bf16_d128_kernel<4>", "avg_launch_us": round(ms["attn_fwd"] * 1e3, 2)},
         "kernels": {
             "attn_fwd": {"workload": fw_name, "avg_us": round(ms["attn_fwd"] * 1e3, 2),
                          "min_us": round(ms_min["attn_fwd"] * 1e3, 2), "tflops": round(fwd_tflops, 2),
@@ -180,7 +201,8 @@ def main():
             "attn_decode_splitkv": {"workload": dw_name, "avg_us": round(ms["attn_decode_splitkv"] * 1e3, 2),
                                     "min_us": round(ms_min["attn_decode_splitkv"] * 1e3, 2),
                                     "gbs": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / acc.PEAK_HBM_GBS, 4),
-                                    "bytes": dw_bytes},
+                                    "bytes": dw_bytes,
+                                    "traffic": None if dec_traffic is None else round(dec_traffic)},
             "online_softmax_rows": {"workload": "softmax_rows_4096x4000",
                                     "avg_us": round(ms["online_softmax_rows"] * 1e3, 2),
                                     "min_us": round(ms_min["online_softmax_rows"] * 1e3, 2),
