@@ -57,6 +57,11 @@ struct Elem<float> {
   }
 };
 
+__device__ __forceinline__ u32x4 nt_load(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ Elem<float>::Vec nt_load(const Elem<float>::Vec* p) {
+  return Elem<float>::Vec{__builtin_nontemporal_load(&p->a), __builtin_nontemporal_load(&p->b)};
+}
+
 // Sum over each aligned group of G lanes (G = 8 or 16) with DPP row ops:
 // xor-1 and xor-2 quad permutes, then mirror within 8, then within 16.
 template <int G>
@@ -113,8 +118,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const T* __
       const int j = base + (u * WAVES + w) * SLOTS + slot;
       jj[u] = j;
       const int js = j < hi ? j : hi - 1;
-      kv[u] = *reinterpret_cast<const Vec*>(Kh + (size_t)js * D + 8 * dc);
-      vv[u] = *reinterpret_cast<const Vec*>(Vh + (size_t)js * D + 8 * dc);
+      kv[u] = nt_load(reinterpret_cast<const Vec*>(Kh + (size_t)js * D + 8 * dc));  // streamed once
+      vv[u] = nt_load(reinterpret_cast<const Vec*>(Vh + (size_t)js * D + 8 * dc));
     }
     float s[kUnroll];
     float mx = kNegInf;

@@ -25,6 +25,9 @@ namespace {
 constexpr int kSmThreads = 256;
 constexpr int kSmWaves = kSmThreads / 64;
 
+// Element access, 4-wide when the row allows it.  ld/st go through the
+// caches; ld_nt/st_nt mark data touched exactly once (non-temporal) so it does
+// not displace data that is reused.
 template <int W>
 __device__ __forceinline__ void ld(const float* p, float* v) {
   if constexpr (W == 4) {
@@ -38,11 +41,23 @@ __device__ __forceinline__ void ld(const float* p, float* v) {
   }
 }
 template <int W>
-__device__ __forceinline__ void st(float* p, const float* v) {
+__device__ __forceinline__ void ld_nt(const float* p, float* v) {
   if constexpr (W == 4) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    v[0] = t[0];
+    v[1] = t[1];
+    v[2] = t[2];
+    v[3] = t[3];
   } else {
-    *p = v[0];
+    v[0] = __builtin_nontemporal_load(p);
+  }
+}
+template <int W>
+__device__ __forceinline__ void st_nt(float* p, const float* v) {
+  if constexpr (W == 4) {
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
+  } else {
+    __builtin_nontemporal_store(v[0], p);
   }
 }
 
@@ -83,7 +98,7 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_reg_kernel(const floa
   for (int i = 0; i < VPT; ++i) {
     const int a = t + kSmThreads * i;
     if (a < nacc) {
-      ld<W>(xr + (size_t)a * W, v[i]);
+      ld_nt<W>(xr + (size_t)a * W, v[i]);
     } else {
 #pragma unroll
       for (int e = 0; e < W; ++e) v[i][e] = kNegInf;
@@ -102,7 +117,7 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_reg_kernel(const floa
       float o[W];
 #pragma unroll
       for (int e = 0; e < W; ++e) o[e] = fast_exp2(fmaf(v[i][e], kLog2e, -r.m)) * inv;
-      st<W>(yr + (size_t)a * W, o);
+      st_nt<W>(yr + (size_t)a * W, o);
     }
   }
 }
@@ -137,10 +152,10 @@ __device__ __forceinline__ void stream_write(const float* xr, float* yr, int nac
   const float inv = 1.0f / r.d;
   for (int a = threadIdx.x; a < nacc; a += kSmThreads) {
     float v[W];
-    ld<W>(xr + (size_t)a * W, v);
+    ld_nt<W>(xr + (size_t)a * W, v);
 #pragma unroll
     for (int e = 0; e < W; ++e) v[e] = fast_exp2(fmaf(v[e], kLog2e, -r.m)) * inv;
-    st<W>(yr + (size_t)a * W, v);
+    st_nt<W>(yr + (size_t)a * W, v);
   }
 }
 
@@ -177,7 +192,8 @@ __device__ __forceinline__ bool better(float xa, int ia, float xb, int ib) {
 template <int W>
 __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x, float* y, float* topv,
                                                                    int32_t* topi, int cols, int k) {
-  constexpr int U = 4;
+  constexpr int U = 8;
+  constexpr int STEP = kSmThreads * U;
   const int row = blockIdx.x;
   const float* xr = x + (size_t)row * cols;
   const int nacc = cols / W;
@@ -190,21 +206,36 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
   int Ti = 0x7fffffff;
   MD r{kNegInf, 0.0f};
 
-  for (int base = 0; base < nacc; base += kSmThreads * U) {
-    float v[U][W];
-    float mx = kNegInf;
+  // Two register buffers used alternately (the loop is unrolled by two so no
+  // buffer is copied): the loads of the next chunk are in flight while the
+  // current one is folded and scanned.  Loads are unconditional (slots past
+  // the row read its first element) and invalid slots become -inf when the
+  // chunk is used, so the load counter can be waited on precisely.
+  float va[U][W], vb[U][W];
+  auto load_chunk = [&](int base, float (&dst)[U][W]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int a = base + threadIdx.x + kSmThreads * u;
-      if (a < nacc) {
-        ld<W>(xr + (size_t)a * W, v[u]);
-      } else {
+      const float* src = xr + (size_t)(a < nacc ? a : 0) * W;
+      if (y)
+        ld<W>(src, dst[u]);  // x is re-read for the full output
+      else
+        ld_nt<W>(src, dst[u]);
+    }
+  };
+
+  auto process = [&](int base, float (&v)[U][W]) {
 #pragma unroll
-        for (int e = 0; e < W; ++e) v[u][e] = kNegInf;
-      }
+    for (int u = 0; u < U; ++u) {
+      const bool ok = base + threadIdx.x + kSmThreads * u < nacc;
+#pragma unroll
+      for (int e = 0; e < W; ++e) v[u][e] = ok ? v[u][e] : kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int e = 0; e < W; ++e) mx = fmaxf(mx, v[u][e]);
-    }
     fold_chunk(r, mx, &v[0][0], U * W);
 
     if (base == 0) {
@@ -225,24 +256,21 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
       }
     }
 
-    bool cand = false;
+    // One ballot per register slot: only lanes whose value in that slot
+    // reaches the threshold are visited, so the cost follows the number of
+    // candidates, not the chunk size.  Slots past the row hold -inf and never
+    // qualify.
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const int a0 = base + w * 64 + kSmThreads * u;  // access index of lane 0
 #pragma unroll
-      for (int e = 0; e < W; ++e) cand = cand || (v[u][e] >= Tx && v[u][e] != kNegInf);
-
-    uint64_t mask = __ballot(cand);
-    while (mask) {
-      const int src = __builtin_ctzll(mask);
-      mask &= mask - 1;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int a_src = base + (w * 64 + src) + kSmThreads * u;
-        if (a_src >= nacc) continue;  // wave-uniform
-#pragma unroll
-        for (int e = 0; e < W; ++e) {
+      for (int e = 0; e < W; ++e) {
+        uint64_t mask = __ballot((v[u][e] >= Tx) & (v[u][e] != kNegInf));
+        while (mask) {
+          const int src = __builtin_ctzll(mask);
+          mask &= mask - 1;
           const float cx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[u][e]), src));
-          const int ci = a_src * W + e;
+          const int ci = (a0 + src) * W + e;
           if (!better(cx, ci, Tx, Ti) && !(cx == Tx && Ti == 0x7fffffff)) continue;  // wave-uniform
           // Insert: lanes whose entry is worse than the candidate take the
           // previous lane's entry, or the candidate if the previous is better.
@@ -268,6 +296,18 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
         }
       }
     }
+  };
+
+  // Chunks are taken in pairs; a pair's second chunk may lie wholly past the
+  // row, in which case all its slots are -inf and it changes nothing.  (An
+  // early exit there would join paths with loads in flight, and the compiler
+  // then waits for all loads at the top of the loop.)
+  load_chunk(0, va);
+  for (int base = 0; base < nacc; base += 2 * STEP) {
+    load_chunk(base + STEP, vb);
+    process(base, va);
+    load_chunk(base + 2 * STEP, va);
+    process(base + STEP, vb);
   }
 
   r = block_md(r);  // contains a __syncthreads
