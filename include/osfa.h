@@ -75,7 +75,7 @@ typedef enum {
  * guard of the same page).
  *
  * scale must be finite and > 0 (typically 1/sqrt(d)).  Supported: d in
- * {64, 128} for both dtypes; B, H, N >= 1; B * H * N * d < 2^40.
+ * {64, 128} for both dtypes; B, H, N >= 1; B * H * N * d < 2^40; N * d < 2^30.
  */
 attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const void* V,
                        void* O, float* LSE, int B, int H, int N, int d, float scale,

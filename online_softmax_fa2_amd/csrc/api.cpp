@@ -46,6 +46,7 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim d=%d not built (64 or 128)", d);
   if ((long long)B * H * N * d >= kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: B*H*N*d too large");
   if ((long long)B * H >= (1LL << 24)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: B*H too large");
+  if ((long long)N * d >= (1LL << 30)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: N*d must be < 2^30 (one head)");
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: scale must be finite and > 0 (got %g)", (double)scale);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: causal must be 0 or 1");

@@ -34,6 +34,8 @@
 // The float32 path follows the same structure with v_mfma_f32_32x32x2f32 and
 // float32 operands in LDS (no transposition needed: each MFMA step consumes
 // one key per 32-lane half).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -381,13 +383,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 inputs, d = 128: direct-to-LDS loads, swizzled LDS, transposed V reads
+// bf16 inputs, d = 128: direct-to-LDS loads, swizzled LDS, transposed V
+// reads, software pipelined across key blocks
 //
 // K and V blocks (64 keys x 256 B each) are copied from global memory into
-// LDS by global_load_lds_dwordx4 (16 B per lane, no VGPR staging), STAGES
-// deep, one barrier per block.  Each load instruction fills 1 KB of LDS =
-// 4 key rows in lane order; the lane fetches whichever 16-byte chunk belongs
-// at its LDS slot under the layout
+// LDS by buffer_load ... lds (16 B per lane, no VGPR staging), one barrier
+// per block.  Each load instruction fills 1 KB of LDS = 4 key rows in lane
+// order; the lane fetches whichever 16-byte chunk belongs at its LDS slot
+// under the layout
 //     byte(row, chunk) = row * 256 + ((chunk ^ f(row)) * 16),
 //     f(row) = ((row & 3) << 2) | ((row >> 2) & 3),
 // an XOR swizzle under which the K-fragment reads (32 rows, one chunk) and
@@ -396,32 +399,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 // lanes, lane i's 4 values from the 4 chunks addressed by lanes 4e + i/4,
 // element i % 4, so that a lane receives 4 consecutive keys of one d column:
 // two such reads form the 8-key A operand of the P V MFMA.
+//
+// One wave's work on consecutive key blocks is overlapped so that the
+// exponentials run while the matrix core is busy:
+//   phase A of step j:  S_{j+1} = K_{j+1} Q^T (MFMA)   with exp of the second
+//                       half of S_j's keys, their row sums and bf16 packing;
+//   phase B of step j:  O += V_j P_j (MFMA)            with the mask and row
+//                       maximum of S_{j+1}, the reference update and the exp
+//                       of the first half of S_{j+1}'s keys.
+// Each phase is written as 16 slots of one MFMA plus a few independent VALU
+// instructions (sched_barrier keeps the slots in order), so the VALU work
+// issues while the MFMA runs.  The factor that rescales the accumulator when
+// the reference moves is applied just before the next P V product (the
+// accumulator is still being written by P_j V_j when the factor is formed);
+// l is rescaled at once.  K and V have separate double buffers: step j reads
+// K_{j+1} and V_j and refills the buffers of K_j and V_{j-1} with K_{j+2} and
+// V_{j+1}.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int kv_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
 
+// Word 3 of a raw buffer resource (gfx9 family: 32-bit data format).
+constexpr int kBufDword3 = 0x00020000;
+// LDS fragment reads are issued this many MFMA slots ahead of their use.
+constexpr int KAHEAD = 4, VAHEAD = 4;
+
 template <int NW>
-__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_bf16_d128_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) {
   constexpr int D = 128;
-  constexpr int BLK_BYTES = kBc * D * 2;         // one K or V block: 16 KB
-  constexpr int STAGE_BYTES = 2 * BLK_BYTES;     // K then V
-  constexpr int LOADS_PER_WAVE = 32 / NW;        // 16 K + 16 V instructions per block
+  constexpr int BLK = kBc * D * 2;  // one K or V block: 16 KB
+  constexpr int LOADS = 16 / NW;    // load instructions per wave per block
   constexpr int NKK = D / 16;
   constexpr int NMD = D / 32;
-  // Two stages as two distinct LDS objects: alias analysis can then tell the
-  // in-flight LDS-DMA writes into one stage from the reads of the other, so
-  // the reads do not wait for the prefetch.
-  __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
+  // Four distinct LDS objects so that alias analysis separates the in-flight
+  // direct-to-LDS writes from the reads of the other buffers.
+  __shared__ __attribute__((aligned(1024))) char k0[BLK];
+  __shared__ __attribute__((aligned(1024))) char k1[BLK];
+  __shared__ __attribute__((aligned(1024))) char v0[BLK];
+  __shared__ __attribute__((aligned(1024))) char v1[BLK];
 
   const Tile tile = map_tile(p);
   if (!tile.valid) return;
   const int b = tile.bh / p.H;
   const int q0 = tile.q0;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
   const int N = p.N;
@@ -435,23 +458,48 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_bf16_d128_kern
   const int kb_hi = (kr.kend > kr.kbeg) ? (kr.kend + kBc - 1) / kBc : kb_lo;
   const int nblk = kb_hi - kb_lo;
 
-  // This wave's share of the 32 load instructions of block kb, into `stage`.
-  auto issue_block = [&](int kb, char* stage) {
+  // This wave's share of the 16 load instructions of one K or V block: load
+  // t fills LDS bytes [1024 i, 1024 i + 1024), i = w + NW t, i.e. key rows
+  // 4 i .. 4 i + 3.  Buffer loads: the head's K (or V) is a buffer resource,
+  // the block start a scalar offset and the lane's byte offset in the block
+  // is fixed.  (Offsets are passed as int, the builtin's parameter type: an
+  // implicit conversion there makes the host pass drop the launch stub.)
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, N * D * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, N * D * 2, kBufDword3);
+  const std::integral_constant<bool, false> kIsK;
+  const std::integral_constant<bool, true> kIsV;
+  int ld_off[LOADS];
 #pragma unroll
-    for (int t = 0; t < LOADS_PER_WAVE; ++t) {
-      const int ii = w + NW * t;
-      const bool isv = ii >= 16;
-      const int i = ii & 15;
-      const int row = 4 * i + (lane >> 4);
-      const int chunk = (lane & 15) ^ swz(row);
-      int j = kb * kBc + row;
-      j = j < N ? j : N - 1;  // rows past N are masked; read a valid row
-      const __bf16* src = (isv ? Vg : Kg) + (size_t)j * D + 8 * chunk;
-      __builtin_amdgcn_global_load_lds(src, stage + (isv ? BLK_BYTES : 0) + i * 1024, 16, 0, 0);
+  for (int t = 0; t < LOADS; ++t) {
+    const int row = 4 * (w + NW * t) + (lane >> 4);
+    ld_off[t] = (row * D + 8 * ((lane & 15) ^ swz(row))) * 2;
+  }
+  auto issue = [&](auto is_v, int kb, char* dst) {
+    const __amdgpu_buffer_rsrc_t rs = decltype(is_v)::value ? vrs : krs;
+    const int soff = kb * kBc * D * 2;
+    if (kb * kBc + kBc <= N) {
+#pragma unroll
+      for (int t = 0; t < LOADS; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (w + NW * t) * 1024),
+                                                 16, (int)ld_off[t], (int)soff, 0, 0);
+    } else {
+      // Last, partial block: rows past N read row N - 1 (they are masked).
+#pragma unroll
+      for (int t = 0; t < LOADS; ++t) {
+        const int row = 4 * (w + NW * t) + (lane >> 4);
+        const int over = kb * kBc + row - (N - 1);
+        const int off = over > 0 ? ld_off[t] - over * D * 2 : ld_off[t];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (w + NW * t) * 1024),
+                                                 16, (int)off, (int)soff, 0, 0);
+      }
     }
   };
 
-  if (nblk > 0) issue_block(kb_lo, lds0);
+  if (nblk > 0) {
+    issue(kIsK, kb_lo, k0);
+    issue(kIsV, kb_lo, v0);
+    if (nblk > 1) issue(kIsK, kb_lo + 1, k1);
+  }
 
   const int qi = q0 + 32 * w + l32;
   bf16x8 qreg[NKK];
@@ -472,115 +520,333 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_bf16_d128_kern
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
   float m_ref = kNegInf;  // reference of l_run and oacc, log2 units
   float l_run = 0.0f;
+  float pend_alpha = 1.0f;  // factor still to be applied to oacc
+  bool pend = false;
   const float c = p.c;
   const int qa = q0 + 32 * w, qb = qa + 31;
   const int krow = perm_key(l32);
-  // V^T transposed-read source address pieces for this lane.
   const int tr_g = lane >> 4, tr_j = lane & 15;
-  const int tr_rowoff = 8 * (tr_g >> 1) + (tr_j >> 2);  // + 16 i + 4 r
-  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_j & 3);   // + 32 md
+  const int tr_rowoff = 8 * (tr_g >> 1) + (tr_j >> 2);
+  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_j & 3);
   const int tr_byte = (tr_j & 1) * 8;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  // One block: wait for its loads, barrier, prefetch the next block into the
-  // other stage, compute from this stage.
-  auto step = [&](int it, const char* cur, char* nxt) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (it + 1 < nblk) issue_block(kb_lo + it + 1, nxt);
-
-    const char* kl = cur;
-    const char* vl = cur + BLK_BYTES;
-    const int j0 = (kb_lo + it) * kBc;
-    if (!rows_see_block(p, kr.jmax, qa, qb, j0)) return;
-
-    f32x16 s[2];
+  // S^T = K Q^T for the block in `kl` (MFMA only, K fragments from LDS).
+  auto scores = [&](const char* kl, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      bf16x8 kf[NKK];
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        kf[kk] = *reinterpret_cast<const bf16x8*>(kl + kv_off(32 * kt + krow, 2 * kk + hf));
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], s[kt], 0, 0, 0);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + kv_off(32 * kt + krow, 2 * kk + hf));
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], s[kt], 0, 0, 0);
+      }
     }
-
-    if (!rows_see_all(p, kr.jmax, qa, qb, j0)) {
+  };
+  // Masks of key block j0 for this lane's query, as a select per score: key
+  // offset t = 32 kt + 16 (r / 8) + 8 hf + r % 8 is visible iff lo < t <= hi.
+  // Each bound is tested only when it cuts into the block for some row of
+  // the wave (a wave-uniform decision), so a causal-diagonal or padding block
+  // costs one compare and one select per score.
+  auto mask = [&](f32x16 (&s)[2], int j0) {
+    if (rows_see_all(p, kr.jmax, qa, qb, j0)) return;
+    int hi = kr.jmax - 1 - j0;                                 // padding: j < jmax
+    int hi_min = hi;                                           // over the wave's rows
+    if (p.causal) {
+      hi = min(hi, qi - j0);                                   // j <= i
+      hi_min = min(hi_min, qa - j0);
+    }
+    int lo = -1 - kBc, lo_max = -1 - kBc;
+    if (p.window > 0) {
+      lo = qi - p.window - j0;                                 // i - j < window
+      lo_max = qb - p.window - j0;
+      if (!p.causal) {
+        hi = min(hi, qi + p.window - 1 - j0);                  // j - i < window
+        hi_min = min(hi_min, qa + p.window - 1 - j0);
+      }
+    }
+    lo -= 8 * hf;
+    hi -= 8 * hf;
+    const bool need_hi = hi_min < kBc - 1, need_lo = lo_max >= 0;
+    if (need_hi && need_lo) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
-          if (!visible(p, kr.jmax, qi, j)) s[kt][r] = kNegInf;
+          const int t = 32 * kt + 16 * (r >> 3) + (r & 7);
+          s[kt][r] = ((t > lo) & (t <= hi)) ? s[kt][r] : kNegInf;
+        }
+    } else if (need_hi) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * kt + 16 * (r >> 3) + (r & 7);
+          s[kt][r] = (t <= hi) ? s[kt][r] : kNegInf;
+        }
+    } else if (need_lo) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * kt + 16 * (r >> 3) + (r & 7);
+          s[kt][r] = (t > lo) ? s[kt][r] : kNegInf;
         }
     }
-
-    float mx = kNegInf;
+  };
+  // Row maximum of a block and the lazy reference update (sets the pending
+  // accumulator factor; l is rescaled here).
+  auto update_ref = [&](const f32x16 (&s)[2]) {
+    float m4[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int q = 0; q < 4; ++q) {
+      float x = fmaxf(s[q >> 1][8 * (q & 1)], s[q >> 1][8 * (q & 1) + 1]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      for (int e = 2; e < 8; e += 2) x = fmaxf(fmaxf(x, s[q >> 1][8 * (q & 1) + e]), s[q >> 1][8 * (q & 1) + e + 1]);
+      m4[q] = x;
+    }
+    const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     const float mblk = max_halves(mx) * c;
     const bool move = mblk > m_ref + kTau;
-    if (__any(move)) {
-      // Lanes that do not move keep alpha = 1 exactly: a lane that has seen
-      // no key yet (m_ref = -inf) must not form exp2(-inf - (-inf)) = NaN.
-      const float alpha = move ? fast_exp2(m_ref - mblk) : 1.0f;  // 0 when moving from -inf
-      const float m_new = move ? mblk : m_ref;
-      l_run *= alpha;
+    // A lane that does not move keeps factor 1 exactly (a lane that has seen
+    // no key must not form exp2(-inf - (-inf))).
+    const float alpha = move ? fast_exp2(m_ref - mblk) : 1.0f;
+    m_ref = move ? mblk : m_ref;
+    l_run *= alpha;
+    pend_alpha = alpha;
+    pend = __any(move);
+  };
+  // exp2 of half a block (the 16 registers of one kt) against the current
+  // reference, packed to bf16; the row sum is taken in float32.
+  auto exp_half = [&](f32x16& s, bf16x8 (&pk)[2]) {
+    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+    float part[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = fast_exp2(fmaf(s[8 * t + e], c, -mr));
+      pk[t] = __builtin_convertvector(f, bf16x8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[t] += f[e];
+    }
+    l_run += part[0] + part[1];
+  };
+  // K fragment i (kt = i / 8, kk = i % 8) of the S^T MFMAs; V^T fragment i
+  // (md = i / 4, 8-key group i % 4) of the P V MFMAs.
+  auto kread = [&](const char* kl, int i) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(kl + kv_off(32 * (i >> 3) + krow, 2 * (i & 7) + hf));
+  };
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  // The swizzle of row 16 g + R (R < 16) equals that of R, so the transposed
+  // reads of group g are those of group 0 moved by 4096 g bytes: 8 per-lane
+  // offsets (r, md) and an immediate per group.
+  int voff[2][NMD];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) voff[r][md] = kv_off(4 * r + tr_rowoff, (32 * md + tr_col) >> 3) + tr_byte;
+  auto vread = [&](const char* vl, int i) -> bf16x8 {
+    const int md = i >> 2, g = i & 3;
+    s16x4 h[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const char* a = vl + voff[r][md] + 4096 * g;
+      h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+    }
+    const s16x8 hv = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8, hv);
+  };
+  // Exponentials of a half block in three stages per pair p of score
+  // registers (2p, 2p + 1), each in its own slot so that no slot waits on a
+  // result of the same slot: the scaled, shifted exponent (in place), the
+  // exp2 (in place), then the bf16 packing into word p of `pw` and the
+  // float32 row-sum.
+  auto st1 = [&](f32x16& s, int p, float mr) {
+    s[2 * p] = fmaf(s[2 * p], c, -mr);
+    s[2 * p + 1] = fmaf(s[2 * p + 1], c, -mr);
+    OSFA_KEEP(s[2 * p]);
+    OSFA_KEEP(s[2 * p + 1]);
+  };
+  auto st2 = [&](f32x16& s, int p) {
+    s[2 * p] = fast_exp2(s[2 * p]);
+    s[2 * p + 1] = fast_exp2(s[2 * p + 1]);
+    OSFA_KEEP(s[2 * p]);
+    OSFA_KEEP(s[2 * p + 1]);
+  };
+  auto st3 = [&](const f32x16& s, int p, u32x4 (&pw)[2], float& acc) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = {s[2 * p], s[2 * p + 1]};
+    uint32_t wd = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    acc += f[0] + f[1];
+    OSFA_KEEP(wd);
+    OSFA_KEEP(acc);
+    pw[p >> 2][p & 3] = wd;
+  };
+  auto to_p = [&](const u32x4 (&pw)[2], bf16x8 (&pk)[2]) {
+    pk[0] = __builtin_bit_cast(bf16x8, pw[0]);
+    pk[1] = __builtin_bit_cast(bf16x8, pw[1]);
+  };
+
+  // One step j: kn holds K_{j+1}, vc holds V_j; kd and vd receive K_{j+2}
+  // and V_{j+1}.  sc = S_j (masked, reference already updated, first half
+  // exponentiated into pc), sn receives S_{j+1}, pn its first-half P.  Each
+  // phase is written as 16 slots of one MFMA plus a few VALU instructions,
+  // with LDS reads issued a fixed number of slots ahead; sched_barrier keeps
+  // the slots in this order.
+  auto step = [&](auto has_next, int j, const char* kn, const char* vc, char* kd, char* vd, f32x16 (&sc)[2],
+                  f32x16 (&sn)[2], const bf16x8 (&pc)[2], bf16x8 (&pn)[2]) {
+    constexpr bool NEXT = decltype(has_next)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if constexpr (NEXT) {
+      if (j + 2 < nblk) issue(kIsK, kb_lo + j + 2, kd);
+      if (j + 1 < nblk) issue(kIsV, kb_lo + j + 1, vd);
+    }
+    // Phase A: S_{j+1} on the matrix core, second half of P_j on the VALU.
+    bf16x8 p1[2];
+    {
+      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+      u32x4 pw[2];
+      float acc = 0.0f;
+      bf16x8 kf[16];
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int i = 0; i < KAHEAD; ++i) kf[i] = kread(kn, i);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (NEXT) {
+          if (i + KAHEAD < 16) kf[i + KAHEAD] = kread(kn, i + KAHEAD);
+          if ((i & 7) == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sn[i >> 3][r] = 0.0f;
+          }
+          sn[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[i & 7], sn[i >> 3], 0, 0, 0);
+        }
+        // Pair p: stage 1 in slot 2p, stage 2 in slot 2p + 1, stage 3 in
+        // slot 2p + 2 (the last one after the loop).
+        if ((i & 1) == 0) st1(sc[1], i >> 1, mr);
+        if (i & 1) st2(sc[1], i >> 1);
+        if ((i & 1) == 0 && i >= 2) st3(sc[1], (i >> 1) - 1, pw, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      st3(sc[1], 7, pw, acc);
+      l_run += acc;
+      to_p(pw, p1);
+    }
+    if constexpr (NEXT) mask(sn, (kb_lo + j + 1) * kBc);
+    // Phase B: P_j V_j on the matrix core; max of S_{j+1}, the reference
+    // update and the first half of P_{j+1} on the VALU.
+    if (pend) {
 #pragma unroll
       for (int md = 0; md < NMD; ++md)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
-      m_ref = m_new;
+        for (int r = 0; r < 16; ++r) oacc[md][r] *= pend_alpha;
     }
-    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
-    float rs = 0.0f;
+    {
+      bf16x8 vf[16];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int i = 0; i < VAHEAD; ++i) vf[i] = vread(vc, i);
+      float m4[4], mx = 0.0f, mblk = 0.0f, alpha = 1.0f;
+      bool move = false;
+      float mr = 0.0f, acc = 0.0f;
+      u32x4 pw[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(s[kt][r], c, -mr));
-        s[kt][r] = e;
-        rs += e;
-      }
-    l_run += rs;
-
-    bf16x8 pb[2][2];
+      for (int i = 0; i < 16; ++i) {
+        if (i + VAHEAD < 16) vf[i + VAHEAD] = vread(vc, i + VAHEAD);
+        const bf16x8 pb = ((i & 3) < 2) ? pc[i & 1] : p1[i & 1];
+        oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pb, oacc[i >> 2], 0, 0, 0);
+        if constexpr (NEXT) {
+          // Row maximum: four independent three-input chains over the
+          // 8-register groups q, one link per slot.
+          if (i == 0) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+            for (int q = 0; q < 4; ++q) {
+              const f32x16& sq = sn[q >> 1];
+              const int o = 8 * (q & 1);
+              m4[q] = fmaxf(fmaxf(sq[o], sq[o + 1]), sq[o + 2]);
+            }
+          } else if (i <= 2) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x8 f;
+            for (int q = 0; q < 4; ++q) {
+              const f32x16& sq = sn[q >> 1];
+              const int o = 8 * (q & 1) + 2 * i + 1;
+              m4[q] = fmaxf(fmaxf(m4[q], sq[o]), sq[o + 1]);
+            }
+          } else if (i == 3) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = s[kt][8 * t + e];
-        pb[kt][t] = __builtin_convertvector(f, bf16x8);
-      }
-
-    // O^T += V^T P^T; V^T fragments by two transposed LDS reads each.
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-#pragma unroll
-    for (int md = 0; md < NMD; ++md) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s16x4 h[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const char* a = vl + kv_off(16 * i + 4 * r + tr_rowoff, (32 * md + tr_col) >> 3) + tr_byte;
-          h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+            for (int q = 0; q < 4; ++q) {
+              m4[q] = fmaxf(m4[q], sn[q >> 1][8 * (q & 1) + 7]);
+            }
+          } else if (i == 4) {
+            mx = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
+          } else if (i == 5) {
+            mblk = max_halves(mx) * c;
+          } else if (i == 6) {
+            move = mblk > m_ref + kTau;
+            // Formed for every lane; lanes that do not move take 1 below
+            // (a lane that has seen no key would form exp2(-inf - (-inf))).
+            alpha = fast_exp2(m_ref - mblk);
+          } else if (i == 7) {
+            alpha = move ? alpha : 1.0f;
+            m_ref = move ? mblk : m_ref;
+            l_run *= alpha;
+            pend_alpha = alpha;
+            pend = __any(move);
+            mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+            OSFA_KEEP(mr);
+            OSFA_KEEP(m_ref);
+            OSFA_KEEP(l_run);
+            OSFA_KEEP(pend_alpha);
+          } else {
+            // Pair k = i - 8: stage 1 now, stage 2 of pair k - 1, stage 3 of
+            // pair k - 2 (the last ones after the loop).
+            const int k = i - 8;
+            st1(sn[0], k, mr);
+            if (k >= 1) st2(sn[0], k - 1);
+            if (k >= 2) st3(sn[0], k - 2, pw, acc);
+          }
         }
-        const s16x8 hv = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hv), pb[i >> 1][i & 1],
-                                                          oacc[md], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (NEXT) {
+        st2(sn[0], 7);
+        st3(sn[0], 6, pw, acc);
+        st3(sn[0], 7, pw, acc);
+        l_run += acc;
+        to_p(pw, pn);
+      } else {
+        pend = false;
       }
     }
   };
 
-  for (int it = 0; it < nblk; it += 2) {
-    step(it, lds0, lds1);
-    if (it + 1 < nblk) step(it + 1, lds1, lds0);
+  if (nblk > 0) {
+    f32x16 sA[2], sB[2];
+    bf16x8 pA[2], pB[2];
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    scores(k0, sA);
+    mask(sA, kb_lo * kBc);
+    update_ref(sA);
+    pend = false;  // the accumulator is still zero
+    exp_half(sA[0], pA);
+    const std::integral_constant<bool, true> yes;
+    const std::integral_constant<bool, false> no;
+    // Steps in pairs (static buffer roles).  When nblk is even, the last
+    // step of the last pair computes scores for the block past the range
+    // from the stale, finite K buffer; the mask sets them all to -inf, so
+    // they change nothing.  An odd nblk ends with one step without a next
+    // block.
+    int j = 0;
+    for (; j + 1 < nblk; j += 2) {
+      step(yes, j, k1, v0, k0, v1, sA, sB, pA, pB);
+      step(yes, j + 1, k0, v1, k1, v0, sB, sA, pB, pA);
+    }
+    if (j < nblk) step(no, j, k1, v0, k0, v1, sA, sB, pA, pB);
   }
 
   const float l_tot = sum_halves(l_run);

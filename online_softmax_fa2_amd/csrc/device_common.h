@@ -124,6 +124,15 @@ __device__ __forceinline__ MD wave_md_merge(MD v) {
   return v;
 }
 
+// Empty register constraint on a value: the code that computes it stays
+// before this point (the compiler may not sink it towards its uses).  The
+// constraint exists only for the device target; the host pass sees nothing.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define OSFA_KEEP(x) asm volatile("" : "+v"(x))
+#else
+#define OSFA_KEEP(x) ((void)0)
+#endif
+
 // bf16 helpers.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

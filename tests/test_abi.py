@@ -75,6 +75,7 @@ def _fwd(lib, **kw):
     (dict(dtype=7), bd.ATTN_ERR_INVALID_ARG, "dtype"),
     (dict(Q=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "aligned"),
     (dict(B=1 << 12, H=1 << 12, N=1 << 12, d=128), bd.ATTN_ERR_INVALID_ARG, "too large"),
+    (dict(N=1 << 23, d=128), bd.ATTN_ERR_INVALID_ARG, "one head"),
 ])
 def test_attn_fwd_rejects(lib, kw, status, msg):
     assert _fwd(lib, **kw) == status
