@@ -52,8 +52,12 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // maximum exceeds it by more than kTau (log2 units), so P = exp2(s - m_ref)
 // stays <= 2^kTau.  Exact: O = A / l and LSE = m_ref + log2 l do not depend on
 // which common reference was used (page "Online softmax for a whole query
-// tile, matrix form", "What interviewers probe next").
-constexpr float kTau = 8.0f;
+// tile, matrix form", "What interviewers probe next").  The reference is
+// always a visible score, so l >= 1 and nothing that matters underflows; P <=
+// 2^32 bounds l by N 2^32 and |A| by N 2^32 max|v|, far inside float32 for
+// N < 2^23 unless |v| > 2^72.  A large threshold makes the rescale of A (64
+// multiplies per lane) rare.
+constexpr float kTau = 32.0f;
 // d = 128 bf16 kernel shape: waves per workgroup.
 constexpr int kV2Waves = 4;
 
@@ -254,7 +258,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
   float m_ref = kNegInf;  // reference of l_run and oacc, log2 units (>= true max - kTau)
-  float l_run = 0.0f;     // this half's share of the running normalizer
+  float l_run = 0.0f;     // this half's share of the running normalizer (float32 P: LSE)
+  float l_bf = 0.0f;      // the same over the bf16 P that enters P V (divides O)
   const float c = p.c;
   const int krow = perm_key(l32);
   const int qa = q0 + 32 * w, qb = qa + 31;  // this wave's query rows
@@ -314,6 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
         const float alpha = move ? fast_exp2(m_ref - mblk) : 1.0f;  // 0 when moving from -inf
         const float m_new = move ? mblk : m_ref;
         l_run *= alpha;
+        l_bf *= alpha;
 #pragma unroll
         for (int md = 0; md < NMD; ++md)
 #pragma unroll
@@ -333,8 +339,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       l_run += rs;
 
       // P^T as the B operand: registers 8t..8t+7 of group kt hold keys
-      // 32 kt + 16 t + 8 hf + [0, 8).
+      // 32 kt + 16 t + 8 hf + [0, 8).  l_bf sums the bf16 P that enters P V.
       bf16x8 pb[2][2];
+      float rb = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -343,7 +350,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[e] = s[kt][8 * t + e];
           pb[kt][t] = __builtin_convertvector(f, bf16x8);
+          const u32x4 w4 = __builtin_bit_cast(u32x4, pb[kt][t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rb = sum_bf16x2(w4[e], rb);
         }
+      l_bf += rb;
 
       // O^T += V^T P^T.
 #pragma unroll
@@ -363,8 +374,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 
   // Epilogue: one division per row (FA2), bf16 O, LSE in natural-log units.
+  // O divides by the sum of the bf16 P it accumulated (their rounding
+  // cancels in the ratio); LSE takes the float32 sum.
   const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float l_div = sum_halves(l_bf);
+  const float inv = l_div > 0.0f ? 1.0f / l_div : 0.0f;
   if (qi < N) {
     __bf16* Og = static_cast<__bf16*>(p.o) + head_off + (size_t)qi * D;
 #pragma unroll
@@ -518,8 +532,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
   for (int md = 0; md < NMD; ++md)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
-  float m_ref = kNegInf;  // reference of l_run and oacc, log2 units
-  float l_run = 0.0f;
+  float m_ref = kNegInf;  // reference of l_run, l_bf and oacc, log2 units
+  float l_run = 0.0f;     // running normalizer over the float32 P (LSE)
+  float l_bf = 0.0f;      // the same over the bf16 P that enters P V (divides O)
   float pend_alpha = 1.0f;  // factor still to be applied to oacc
   bool pend = false;
   const float c = p.c;
@@ -544,55 +559,63 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
       }
     }
   };
-  // Masks of key block j0 for this lane's query, as a select per score: key
-  // offset t = 32 kt + 16 (r / 8) + 8 hf + r % 8 is visible iff lo < t <= hi.
-  // Each bound is tested only when it cuts into the block for some row of
-  // the wave (a wave-uniform decision), so a causal-diagonal or padding block
-  // costs one compare and one select per score.
+  // Masks of key block j0 for this lane's query: key offset
+  // t = 32 kt + 16 (r / 8) + 8 hf + r % 8 is visible iff lo < t <= hi.
+  // Decided per 32-key half kt from the bounds' extremes over the wave's
+  // rows (wave-uniform): a half that every row sees fully is left alone, a
+  // half that no row sees is set to -inf, and only a half that a bound cuts
+  // into takes a compare and a select per score.  Query tiles start at
+  // multiples of 32, so a causal diagonal or a window edge cuts into one half.
   auto mask = [&](f32x16 (&s)[2], int j0) {
     if (rows_see_all(p, kr.jmax, qa, qb, j0)) return;
     int hi = kr.jmax - 1 - j0;                                 // padding: j < jmax
-    int hi_min = hi;                                           // over the wave's rows
+    int hi_min = hi, hi_max = hi;                              // over the wave's rows
     if (p.causal) {
       hi = min(hi, qi - j0);                                   // j <= i
       hi_min = min(hi_min, qa - j0);
+      hi_max = min(hi_max, qb - j0);
     }
-    int lo = -1 - kBc, lo_max = -1 - kBc;
+    int lo = -1 - kBc, lo_min = -1 - kBc, lo_max = -1 - kBc;
     if (p.window > 0) {
       lo = qi - p.window - j0;                                 // i - j < window
+      lo_min = qa - p.window - j0;
       lo_max = qb - p.window - j0;
       if (!p.causal) {
         hi = min(hi, qi + p.window - 1 - j0);                  // j - i < window
         hi_min = min(hi_min, qa + p.window - 1 - j0);
+        hi_max = min(hi_max, qb + p.window - 1 - j0);
       }
     }
     lo -= 8 * hf;
     hi -= 8 * hf;
-    const bool need_hi = hi_min < kBc - 1, need_lo = lo_max >= 0;
-    if (need_hi && need_lo) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      const int t0 = 32 * kt, t1 = 32 * kt + 31;
+      if (hi_max < t0 || lo_min >= t1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = kNegInf;
+        continue;
+      }
+      const bool need_hi = hi_min < t1, need_lo = lo_max >= t0;
+      if (need_hi && need_lo) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int t = 32 * kt + 16 * (r >> 3) + (r & 7);
+          const int t = t0 + 16 * (r >> 3) + (r & 7);
           s[kt][r] = ((t > lo) & (t <= hi)) ? s[kt][r] : kNegInf;
         }
-    } else if (need_hi) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      } else if (need_hi) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int t = 32 * kt + 16 * (r >> 3) + (r & 7);
+          const int t = t0 + 16 * (r >> 3) + (r & 7);
           s[kt][r] = (t <= hi) ? s[kt][r] : kNegInf;
         }
-    } else if (need_lo) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      } else if (need_lo) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int t = 32 * kt + 16 * (r >> 3) + (r & 7);
+          const int t = t0 + 16 * (r >> 3) + (r & 7);
           s[kt][r] = (t > lo) ? s[kt][r] : kNegInf;
         }
+      }
     }
   };
   // Row maximum of a block and the lazy reference update (sets the pending
@@ -614,6 +637,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     const float alpha = move ? fast_exp2(m_ref - mblk) : 1.0f;
     m_ref = move ? mblk : m_ref;
     l_run *= alpha;
+    l_bf *= alpha;
     pend_alpha = alpha;
     pend = __any(move);
   };
@@ -630,6 +654,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
       pk[t] = __builtin_convertvector(f, bf16x8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) part[t] += f[e];
+      const u32x4 w4 = __builtin_bit_cast(u32x4, pk[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l_bf = sum_bf16x2(w4[e], l_bf);
     }
     l_run += part[0] + part[1];
   };
@@ -676,13 +703,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     OSFA_KEEP(s[2 * p]);
     OSFA_KEEP(s[2 * p + 1]);
   };
-  auto st3 = [&](const f32x16& s, int p, u32x4 (&pw)[2], float& acc) {
+  auto st3 = [&](const f32x16& s, int p, u32x4 (&pw)[2], float& acc, float& accb) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     const f32x2 f = {s[2 * p], s[2 * p + 1]};
     uint32_t wd = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
     acc += f[0] + f[1];
+    accb = sum_bf16x2(wd, accb);
     OSFA_KEEP(wd);
     OSFA_KEEP(acc);
+    OSFA_KEEP(accb);
     pw[p >> 2][p & 3] = wd;
   };
   auto to_p = [&](const u32x4 (&pw)[2], bf16x8 (&pk)[2]) {
@@ -710,7 +739,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     {
       const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
       u32x4 pw[2];
-      float acc = 0.0f;
+      float acc = 0.0f, accb = 0.0f;
       bf16x8 kf[16];
       if constexpr (NEXT) {
 #pragma unroll
@@ -730,11 +759,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
         // slot 2p + 2 (the last one after the loop).
         if ((i & 1) == 0) st1(sc[1], i >> 1, mr);
         if (i & 1) st2(sc[1], i >> 1);
-        if ((i & 1) == 0 && i >= 2) st3(sc[1], (i >> 1) - 1, pw, acc);
+        if ((i & 1) == 0 && i >= 2) st3(sc[1], (i >> 1) - 1, pw, acc, accb);
         __builtin_amdgcn_sched_barrier(0);
       }
-      st3(sc[1], 7, pw, acc);
+      st3(sc[1], 7, pw, acc, accb);
       l_run += acc;
+      l_bf += accb;
       to_p(pw, p1);
     }
     if constexpr (NEXT) mask(sn, (kb_lo + j + 1) * kBc);
@@ -752,7 +782,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
       for (int i = 0; i < VAHEAD; ++i) vf[i] = vread(vc, i);
       float m4[4], mx = 0.0f, mblk = 0.0f, alpha = 1.0f;
       bool move = false;
-      float mr = 0.0f, acc = 0.0f;
+      float mr = 0.0f, acc = 0.0f, accb = 0.0f;
       u32x4 pw[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -794,6 +824,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
             alpha = move ? alpha : 1.0f;
             m_ref = move ? mblk : m_ref;
             l_run *= alpha;
+            l_bf *= alpha;
             pend_alpha = alpha;
             pend = __any(move);
             mr = (m_ref == kNegInf) ? 0.0f : m_ref;
@@ -807,16 +838,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
             const int k = i - 8;
             st1(sn[0], k, mr);
             if (k >= 1) st2(sn[0], k - 1);
-            if (k >= 2) st3(sn[0], k - 2, pw, acc);
+            if (k >= 2) st3(sn[0], k - 2, pw, acc, accb);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (NEXT) {
         st2(sn[0], 7);
-        st3(sn[0], 6, pw, acc);
-        st3(sn[0], 7, pw, acc);
+        st3(sn[0], 6, pw, acc, accb);
+        st3(sn[0], 7, pw, acc, accb);
         l_run += acc;
+        l_bf += accb;
         to_p(pw, pn);
       } else {
         pend = false;
@@ -849,8 +881,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     if (j < nblk) step(no, j, k1, v0, k0, v1, sA, sB, pA, pB);
   }
 
+  // O divides by the sum of the bf16 P it accumulated (their rounding
+  // cancels in the ratio); LSE takes the float32 sum.
   const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float l_div = sum_halves(l_bf);
+  const float inv = l_div > 0.0f ? 1.0f / l_div : 0.0f;
   if (qi < N) {
     __bf16* Og = static_cast<__bf16*>(p.o) + head_off + (size_t)qi * D;
 #pragma unroll

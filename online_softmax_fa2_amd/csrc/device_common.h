@@ -134,6 +134,13 @@ __device__ __forceinline__ MD wave_md_merge(MD v) {
 #endif
 
 // bf16 helpers.
+// acc + lo + hi of a packed pair of bf16 values (v_dot2_f32_bf16 against
+// (1, 1), float32 accumulate).
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
