@@ -868,17 +868,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     exp_half(sA[0], pA);
     const std::integral_constant<bool, true> yes;
     const std::integral_constant<bool, false> no;
-    // Steps in pairs (static buffer roles).  When nblk is even, the last
-    // step of the last pair computes scores for the block past the range
-    // from the stale, finite K buffer; the mask sets them all to -inf, so
-    // they change nothing.  An odd nblk ends with one step without a next
-    // block.
+    // Steps in pairs (static buffer roles); the last step has no next block.
     int j = 0;
-    for (; j + 1 < nblk; j += 2) {
+    for (; j + 2 < nblk; j += 2) {
       step(yes, j, k1, v0, k0, v1, sA, sB, pA, pB);
       step(yes, j + 1, k0, v1, k1, v0, sB, sA, pB, pA);
     }
-    if (j < nblk) step(no, j, k1, v0, k0, v1, sA, sB, pA, pB);
+    if (j + 1 < nblk) {
+      step(yes, j, k1, v0, k0, v1, sA, sB, pA, pB);
+      step(no, j + 1, k0, v1, k1, v0, sB, sA, pB, pA);
+    } else {
+      step(no, j, k1, v0, k0, v1, sA, sB, pA, pB);
+    }
   }
 
   // O divides by the sum of the bf16 P it accumulated (their rounding
