@@ -188,8 +188,18 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_stream_kernel(const f
 __device__ __forceinline__ bool better(float xa, int ia, float xb, int ib) {
   return xa > xb || (xa == xb && ia < ib);
 }
+// Float order as signed-int order (for LDS integer max), and back.
+__device__ __forceinline__ int ord_f(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float unord_f(int b) { return __builtin_bit_cast(float, b >= 0 ? b : b ^ 0x7fffffff); }
 
-template <int W>
+// WITH_Y: the full output y is written too (a second pass re-reads x, so the
+// first pass keeps x in the caches); without it x is read once, non-temporal.
+// (Two instantiations: with a run-time test the compiler merges the two
+// loads into one and drops the non-temporal hint.)
+template <int W, bool WITH_Y>
 __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x, float* y, float* topv,
                                                                    int32_t* topi, int cols, int k) {
   constexpr int U = 8;
@@ -205,6 +215,13 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
   float Tx = kNegInf;  // wave-uniform threshold
   int Ti = 0x7fffffff;
   MD r{kNegInf, 0.0f};
+  // The largest of the 4 waves' thresholds, as an order-preserving int (any
+  // wave's k-th entry bounds the row's k-th value from below, so elements
+  // under it are skipped by every wave).  Read and raised without a barrier:
+  // a stale value is still a valid bound.
+  __shared__ int t_shared;
+  if (threadIdx.x == 0) t_shared = ord_f(kNegInf);
+  __syncthreads();
 
   // Two register buffers used alternately (the loop is unrolled by two so no
   // buffer is copied): the loads of the next chunk are in flight while the
@@ -217,8 +234,8 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
     for (int u = 0; u < U; ++u) {
       const int a = base + threadIdx.x + kSmThreads * u;
       const float* src = xr + (size_t)(a < nacc ? a : 0) * W;
-      if (y)
-        ld<W>(src, dst[u]);  // x is re-read for the full output
+      if constexpr (WITH_Y)
+        ld<W>(src, dst[u]);
       else
         ld_nt<W>(src, dst[u]);
     }
@@ -256,6 +273,11 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
       }
     }
 
+    // Publish this wave's threshold, take the workgroup's.
+    if (lane == 0 && Tx != kNegInf) atomicMax(&t_shared, ord_f(Tx));
+    const float Tf = fmaxf(Tx, unord_f(__builtin_amdgcn_readfirstlane(t_shared)));
+    // Nothing in the chunk reaches the threshold: no slot needs a look.
+    if (__ballot((mx >= Tf) & (mx != kNegInf)) == 0) return;
     // One ballot per register slot: only lanes whose value in that slot
     // reaches the threshold are visited, so the cost follows the number of
     // candidates, not the chunk size.  Slots past the row hold -inf and never
@@ -265,7 +287,7 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
       const int a0 = base + w * 64 + kSmThreads * u;  // access index of lane 0
 #pragma unroll
       for (int e = 0; e < W; ++e) {
-        uint64_t mask = __ballot((v[u][e] >= Tx) & (v[u][e] != kNegInf));
+        uint64_t mask = __ballot((v[u][e] >= fmaxf(Tx, Tf)) & (v[u][e] != kNegInf));
         while (mask) {
           const int src = __builtin_ctzll(mask);
           mask &= mask - 1;
@@ -329,7 +351,7 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
       topi[(size_t)row * k + rank] = mi;
     }
   }
-  if (y) stream_write<W>(xr, y + (size_t)row * cols, nacc, r);
+  if constexpr (WITH_Y) stream_write<W>(xr, y + (size_t)row * cols, nacc, r);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -366,10 +388,14 @@ hipError_t launch_softmax_topk(const float* x, float* y, float* topv, int32_t* t
                                hipStream_t stream) {
   const bool vec = (cols % 4 == 0) && aligned16(x) && (y == nullptr || aligned16(y));
   const dim3 grid(rows), block(kSmThreads);
-  if (vec)
-    hipLaunchKernelGGL((softmax_topk_kernel<4>), grid, block, 0, stream, x, y, topv, topi, cols, k);
+  if (vec && y)
+    hipLaunchKernelGGL((softmax_topk_kernel<4, true>), grid, block, 0, stream, x, y, topv, topi, cols, k);
+  else if (vec)
+    hipLaunchKernelGGL((softmax_topk_kernel<4, false>), grid, block, 0, stream, x, y, topv, topi, cols, k);
+  else if (y)
+    hipLaunchKernelGGL((softmax_topk_kernel<1, true>), grid, block, 0, stream, x, y, topv, topi, cols, k);
   else
-    hipLaunchKernelGGL((softmax_topk_kernel<1>), grid, block, 0, stream, x, y, topv, topi, cols, k);
+    hipLaunchKernelGGL((softmax_topk_kernel<1, false>), grid, block, 0, stream, x, y, topv, topi, cols, k);
   return hipGetLastError();
 }
 
