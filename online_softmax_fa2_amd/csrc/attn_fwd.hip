@@ -730,10 +730,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     constexpr bool NEXT = decltype(has_next)::value;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if constexpr (NEXT) {
-      if (j + 2 < nblk) issue(kIsK, kb_lo + j + 2, kd);
-      if (j + 1 < nblk) issue(kIsV, kb_lo + j + 1, vd);
-    }
+    // (A wave that does not see block j + 1 runs this step without NEXT but
+    // still loads its share of V_{j+1} for the others.)
+    if (j + 2 < nblk) issue(kIsK, kb_lo + j + 2, kd);
+    if (j + 1 < nblk) issue(kIsV, kb_lo + j + 1, vd);
     // Phase A: S_{j+1} on the matrix core, second half of P_j on the VALU.
     bf16x8 p1[2];
     {
@@ -861,8 +861,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     bf16x8 pA[2], pB[2];
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    scores(k0, sA);
-    mask(sA, kb_lo * kBc);
+    // A wave skips the matrix work of the range's first or last block when
+    // none of its 32 rows sees it (a window edge, a causal diagonal).
+    if (rows_see_block(p, kr.jmax, qa, qb, kb_lo * kBc)) {
+      scores(k0, sA);
+      mask(sA, kb_lo * kBc);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sA[kt][r] = kNegInf;
+    }
     update_ref(sA);
     pend = false;  // the accumulator is still zero
     exp_half(sA[0], pA);
@@ -874,11 +883,26 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
       step(yes, j, k1, v0, k0, v1, sA, sB, pA, pB);
       step(yes, j + 1, k0, v1, k1, v0, sB, sA, pB, pA);
     }
+    // The last block: a wave that sees none of it neither scores it (the
+    // step before runs without a next block) nor multiplies it with V (its
+    // step is only the barrier every wave takes).
+    const bool see_last = rows_see_block(p, kr.jmax, qa, qb, (kb_lo + nblk - 1) * kBc);
+    auto barrier_step = [&]() {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    };
     if (j + 1 < nblk) {
-      step(yes, j, k1, v0, k0, v1, sA, sB, pA, pB);
-      step(no, j + 1, k0, v1, k1, v0, sB, sA, pB, pA);
-    } else {
+      if (see_last) {
+        step(yes, j, k1, v0, k0, v1, sA, sB, pA, pB);
+        step(no, j + 1, k0, v1, k1, v0, sB, sA, pB, pA);
+      } else {
+        step(no, j, k1, v0, k0, v1, sA, sB, pA, pB);
+        barrier_step();
+      }
+    } else if (see_last) {
       step(no, j, k1, v0, k0, v1, sA, sB, pA, pB);
+    } else {
+      barrier_step();
     }
   }
 
