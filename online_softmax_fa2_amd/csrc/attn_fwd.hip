@@ -624,12 +624,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     float m4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float x = fmaxf(s[q >> 1][8 * (q & 1)], s[q >> 1][8 * (q & 1) + 1]);
-#pragma unroll
-      for (int e = 2; e < 8; e += 2) x = fmaxf(fmaxf(x, s[q >> 1][8 * (q & 1) + e]), s[q >> 1][8 * (q & 1) + e + 1]);
-      m4[q] = x;
+      const f32x16& sq = s[q >> 1];
+      const int o = 8 * (q & 1);
+      m4[q] = vmax3(vmax3(vmax3(sq[o], sq[o + 1], sq[o + 2]), sq[o + 3], sq[o + 4]), sq[o + 5], sq[o + 6]);
     }
-    const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    const float mx = vmax3(vmax3(m4[0], m4[1], s[0][7]), vmax3(m4[2], m4[3], s[0][15]), vmax(s[1][7], s[1][15]));
     const float mblk = max_halves(mx) * c;
     const bool move = mblk > m_ref + kTau;
     // A lane that does not move keeps factor 1 exactly (a lane that has seen
@@ -790,29 +789,29 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
         const bf16x8 pb = ((i & 3) < 2) ? pc[i & 1] : p1[i & 1];
         oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pb, oacc[i >> 2], 0, 0, 0);
         if constexpr (NEXT) {
-          // Row maximum: four independent three-input chains over the
-          // 8-register groups q, one link per slot.
+          // Row maximum of the 32 scores in 16 three-input maxima: four
+          // independent chains over the 8-register groups q, one link per
+          // slot, then the four chains and their last registers.
           if (i == 0) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const f32x16& sq = sn[q >> 1];
               const int o = 8 * (q & 1);
-              m4[q] = fmaxf(fmaxf(sq[o], sq[o + 1]), sq[o + 2]);
+              m4[q] = vmax3(sq[o], sq[o + 1], sq[o + 2]);
             }
           } else if (i <= 2) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const f32x16& sq = sn[q >> 1];
               const int o = 8 * (q & 1) + 2 * i + 1;
-              m4[q] = fmaxf(fmaxf(m4[q], sq[o]), sq[o + 1]);
+              m4[q] = vmax3(m4[q], sq[o], sq[o + 1]);
             }
           } else if (i == 3) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              m4[q] = fmaxf(m4[q], sn[q >> 1][8 * (q & 1) + 7]);
-            }
+            m4[0] = vmax3(m4[0], m4[1], sn[0][7]);
+            m4[2] = vmax3(m4[2], m4[3], sn[0][15]);
+            m4[1] = vmax(sn[1][7], sn[1][15]);
           } else if (i == 4) {
-            mx = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
+            mx = vmax3(m4[0], m4[2], m4[1]);
           } else if (i == 5) {
             mblk = max_halves(mx) * c;
           } else if (i == 6) {
