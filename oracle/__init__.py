@@ -8,6 +8,7 @@ from the product path: the two share no code.
 
 Modules
   attention -- the direct definition of softmax attention (masked), decode.
+  backward  -- the gradients dQ, dK, dV of masked softmax attention.
   softmax   -- the direct definition of row softmax and its top-k.
   models    -- the pages' streaming algorithms (per-element (m, d) update,
                the associative merge, the single-query and query-tile
@@ -17,8 +18,9 @@ Modules
 
 Every function states the passage of the pages it follows.  The pages are
 cited by title: "Derive online softmax, prove it is exact" (the single-query
-derivation), "Online softmax for a whole query tile, matrix form" (the tile
-form, masks, the guard, FA2's deferred division) and "Online softmax" (the
+derivation, the backward pass's recomputation from the log-sum-exp),
+"Online softmax for a whole query tile, matrix form" (the tile form, masks,
+the guard, FA2's deferred division) and "Online softmax" (the
 article on Milakov and Gimelshein's online normalizer: Steps 1-4, the worked
 example, trade-offs).
 
@@ -29,3 +31,4 @@ invariants and brute force.  No function is "parity unpinned".
 
 from .attention import attention_ref, decode_ref, visible_mask, visible_count  # noqa: F401
 from .softmax import softmax_ref, topk_ref  # noqa: F401
+from .backward import attention_bwd_ref, attention_bwd_delta  # noqa: F401
