@@ -8,7 +8,8 @@ from the product path: the two share no code.
 
 Modules
   attention -- the direct definition of softmax attention (masked), decode.
-  backward  -- the gradients dQ, dK, dV of masked softmax attention.
+  backward  -- the gradients dQ, dK, dV of masked softmax attention, and a
+               first-order bound on their rounding error (a tolerance).
   softmax   -- the direct definition of row softmax and its top-k.
   models    -- the pages' streaming algorithms (per-element (m, d) update,
                the associative merge, the single-query and query-tile
@@ -31,4 +32,4 @@ invariants and brute force.  No function is "parity unpinned".
 
 from .attention import attention_ref, decode_ref, visible_mask, visible_count  # noqa: F401
 from .softmax import softmax_ref, topk_ref  # noqa: F401
-from .backward import attention_bwd_ref, attention_bwd_delta  # noqa: F401
+from .backward import attention_bwd_ref, attention_bwd_delta, attention_bwd_error_bound  # noqa: F401

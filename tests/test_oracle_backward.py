@@ -117,3 +117,95 @@ def test_delta_is_row_sum_of_p_times_dp():
     p = ob._probs(Q[0, 0], K[0, 0], sigma, idx[None, :] <= idx[:, None])
     dp = dO[0, 0] @ V[0, 0].T
     assert np.max(np.abs(D - (p * dp).sum(axis=1))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# The rounding-error bound used as the GPU tolerance: it must cover a
+# simulated bf16 pipeline (O, P, dS and the outputs rounded to bf16 with
+# round-to-nearest-even, everything else exact), every one of its terms must
+# be needed, and it must not be vacuous.
+# ---------------------------------------------------------------------------
+
+def _bf(x):
+    from online_softmax_fa2_amd.inputs import bf16_round
+    return bf16_round(np.asarray(x, np.float32))[1].astype(np.float64)
+
+
+def _sim_bf16_bwd(Q, K, V, dO, scale, m, mistake=None):
+    """The bf16 pipeline, optionally with one planted mistake (to show the bound would catch it)."""
+    B, H, N, d = Q.shape
+    sigma = float(np.float32(scale))
+    out = [np.zeros((B, H, N, d)) for _ in range(3)]
+    idx = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            klen = N if m["kv_len"] is None else m["kv_len"][b]
+            q, k, v, g = Q[b, h], K[b, h], V[b, h], dO[b, h]
+            vis = ob.visible_mask(idx, idx, N, klen, m["causal"], m["window"])
+            if mistake == "mask_off_by_one":
+                vis = ob.visible_mask(idx, idx, N, klen - 1, m["causal"], m["window"] + (m["window"] > 0))
+            p = ob._probs(q, k, sigma, vis)
+            o = _bf(p @ v)
+            dp = g @ v.T
+            dd = (g * o).sum(axis=1, keepdims=True)
+            if mistake == "no_delta":
+                dd = 0.0 * dd
+            ds = _bf(p * (dp - dd))
+            if mistake == "ds_transposed_block":
+                ds[:32, :32] = ds[:32, :32].T.copy()
+            out[0][b, h] = _bf(sigma * (ds @ k))
+            out[1][b, h] = _bf((1.0 if mistake == "dk_unscaled" else sigma) * (ds.T @ q))
+            out[2][b, h] = _bf(_bf(p).T @ g)
+    return out
+
+
+def _bf_inputs(N, d, seed, big=()):
+    Q, K, V, dO = (_bf(_rand((1, 1, N, d), seed + i)) for i in range(4))
+    K[:, :, list(big), :] *= 8.0
+    return Q, K, V, dO
+
+
+@pytest.mark.parametrize("big", [(), (3, 77, 120)], ids=["plain", "big_keys"])
+@pytest.mark.parametrize("m", MASKS[:-1] + [dict(causal=True, window=40, kv_len=[100])], ids=str)
+def test_bound_covers_simulated_bf16(m, big):
+    """The bound holds for every element, and four plausible mistakes each break it."""
+    Q, K, V, dO = _bf_inputs(160, 16, 40, big=big)
+    sc = 0.25
+    ref = attention_bwd_ref(Q, K, V, dO, sc, **m)
+    bnd = ob.attention_bwd_error_bound(Q, K, V, dO, sc, **m)
+    sim = _sim_bf16_bwd(Q, K, V, dO, sc, m)
+    for name, s, r, bd in zip("QKV", sim, ref, bnd):
+        assert np.all(np.abs(s - r) <= 1.01 * bd + 1e-300), f"d{name}: simulated error exceeds the bound"
+    # Not vacuous: each planted mistake escapes it.
+    for mistake in ("no_delta", "mask_off_by_one", "ds_transposed_block", "dk_unscaled"):
+        bad = _sim_bf16_bwd(Q, K, V, dO, sc, m, mistake)
+        assert any(np.any(np.abs(s - r) > 1.01 * bd) for s, r, bd in zip(bad, ref, bnd)), mistake
+
+
+def test_bound_terms_are_needed():
+    """Drop the D term or the operand term (planted mistakes in the bound) and the simulated error escapes it.
+
+    (The output-rounding term is kept for rigour; with the worst-case sums of
+    the other two it is never the one that decides.)
+    """
+    m = dict(causal=False, window=0, kv_len=None)
+    Q, K, V, dO = _bf_inputs(160, 16, 41, big=(5, 90))
+    sc = 0.25
+    ref = attention_bwd_ref(Q, K, V, dO, sc, **m)
+    sim = _sim_bf16_bwd(Q, K, V, dO, sc, m)
+
+    def escapes(**u):
+        bnd = ob.attention_bwd_error_bound(Q, K, V, dO, sc, **m, **u)
+        return [bool(np.any(np.abs(s - r) > 1.01 * bd)) for s, r, bd in zip(sim, ref, bnd)]
+
+    assert escapes() == [False, False, False]
+    assert escapes(u_o=0.0)[0]                # D's rounding reaches dQ
+    assert escapes(u_operand=0.0)[2]          # P's rounding reaches dV
+
+
+def test_bound_zero_where_gradient_vanishes():
+    m = dict(causal=True, window=2, kv_len=[2])
+    Q, K, V, dO = _bf_inputs(8, 4, 42)
+    bQ, bK, bV = ob.attention_bwd_error_bound(Q, K, V, dO, 0.5, **m)
+    assert np.all(bQ[0, 0, 3:] == 0)          # queries 3.. see no key
+    assert np.all(bK[0, 0, 2:] == 0) and np.all(bV[0, 0, 2:] == 0)  # keys 2.. are padding
