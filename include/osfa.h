@@ -82,6 +82,41 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
                        int causal, int window, const int32_t* kv_len, hipStream_t stream);
 
 /*
+ * attn_bwd_workspace_bytes -- bytes of device workspace that attn_bwd needs:
+ * 2 * B * H * N * 4 (per query, D = rowsum(dO * O) and LSE in log2 units,
+ * float32).  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * attn_bwd -- backward pass of attn_fwd: the gradients dQ, dK, dV of the
+ * forward output O for an incoming gradient dO.
+ *
+ * The forward's per-row log-sum-exp is all that is kept: P is recomputed
+ * block by block from Q, K and LSE as the normalized P = exp(scale Q K^T -
+ * LSE), with no running maximum (page "Derive online softmax, prove it is
+ * exact", "What interviewers probe next"; page "Online softmax for a whole
+ * query tile, matrix form", "What interviewers probe next").  With
+ * D_i = sum_d dO_id O_id,
+ *   dV = P^T dO,   dS = P * (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q,
+ * over the same visible pairs as attn_fwd (same causal / window / kv_len
+ * arguments and the same reading of them).  A query that sees no key (LSE =
+ * -inf) contributes nothing.
+ *
+ * Layout: Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] bf16, d fastest; LSE
+ * is [B, H, N] float32 as written by attn_fwd for the same Q, K, V.  dQ, dK,
+ * dV are fully overwritten (rounded to nearest even).  workspace:
+ * caller-owned device memory of at least attn_bwd_workspace_bytes(B, H, N)
+ * bytes, 4-byte aligned; its contents on return are unspecified.
+ * Supported: dtype ATTN_BF16 and d = 128 (others -> ATTN_ERR_UNSUPPORTED);
+ * B, H, N >= 1; B * H * N * d < 2^40; N * d < 2^30.
+ */
+attn_status_t attn_bwd(attn_dtype_t dtype, const void* Q, const void* K, const void* V, const void* O,
+                       const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N,
+                       int d, float scale, int causal, int window, const int32_t* kv_len, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_decode_splitkv_workspace_bytes -- bytes of device workspace that
  * attn_decode_splitkv needs: B * H * nsplit * (d + 2) * 4 (one partial
  * (m, l, a[d]) triple per split, float32).  Returns 0 for invalid sizes.

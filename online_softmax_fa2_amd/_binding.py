@@ -39,6 +39,10 @@ def load_library() -> ctypes.CDLL:
     p, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [i, p, p, p, p, p, i, i, i, i, f, i, i, p, p]
     lib.attn_fwd.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd.argtypes = [i, p, p, p, p, p, p, p, p, p, i, i, i, i, f, i, i, p, p, sz, p]
+    lib.attn_bwd.restype = i
     lib.attn_decode_splitkv_workspace_bytes.argtypes = [i, i, i, i]
     lib.attn_decode_splitkv_workspace_bytes.restype = sz
     lib.attn_decode_splitkv.argtypes = [i, p, p, p, p, i, i, i, i, i, p, sz, p]
@@ -99,6 +103,38 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, window: 
     _check(load_library().attn_fwd(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                                    float(scale), int(bool(causal)), int(window), _ptr(kv_len), _stream(stream)))
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, H, N))
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False, window: int = 0,
+             kv_len=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dQ, dK, dV) of attention for [B, H, N, d] bf16 tensors, given O and LSE from attn_fwd."""
+    _need_device(q, k, v, o, dout, lse, kv_len, dq, dk, dv, workspace)
+    if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must share one dtype")
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must all be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N):
+        raise ValueError("lse must be float32 [B, H, N]")
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B):
+        raise ValueError("kv_len must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    _check(load_library().attn_bwd(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                                   int(window), _ptr(kv_len), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
 
 
 def decode_workspace_bytes(B: int, H: int, d: int, nsplit: int) -> int:

@@ -58,6 +58,41 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
   return hip_status(e, "attn_fwd");
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return 2 * (size_t)B * H * N * sizeof(float);
+}
+
+attn_status_t attn_bwd(attn_dtype_t dtype, const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                       const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d, float scale,
+                       int causal, int window, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: unknown dtype %d", (int)dtype);
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: null pointer");
+  if (B < 1 || H < 1 || N < 1 || d < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: sizes must be >= 1 (B=%d H=%d N=%d d=%d)", B, H, N, d);
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: only bf16 is built");
+  if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: head dim d=%d not built (128)", d);
+  if ((long long)B * H * N * d >= kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: B*H*N*d too large");
+  if ((long long)B * H >= (1LL << 24)) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: B*H too large");
+  if ((long long)N * d >= (1LL << 30)) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: N*d must be < 2^30 (one head)");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: scale must be finite and > 0 (got %g)", (double)scale);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: causal must be 0 or 1");
+  if (window < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: window must be >= 0 (0 = no window)");
+  const size_t need = attn_bwd_workspace_bytes(B, H, N);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK |
+       (uintptr_t)dV) & 15)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned");
+  if (((uintptr_t)LSE | (uintptr_t)workspace) & 3)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: LSE and workspace must be 4-byte aligned");
+  osfa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, kv_len, static_cast<float*>(workspace), B, H, N, d, scale, causal, window};
+  return hip_status(osfa::launch_attn_bwd_bf16(a, stream), "attn_bwd");
+}
+
 size_t attn_decode_splitkv_workspace_bytes(int B, int H, int d, int nsplit) {
   if (B < 1 || H < 1 || d < 1 || nsplit < 1) return 0;
   return (size_t)B * H * nsplit * (size_t)(d + 2) * sizeof(float);

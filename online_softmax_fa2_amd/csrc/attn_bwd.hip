@@ -1,0 +1,592 @@
+// Attention backward pass for gfx950 (bf16, d = 128): the gradients dQ, dK,
+// dV of the forward output, with P recomputed block by block from Q, K and
+// the per-row log-sum-exp the forward wrote, normalized directly as
+// P = exp(S - LSE) with no running maximum (page "Derive online softmax,
+// prove it is exact", "What interviewers probe next"; page "Online softmax
+// for a whole query tile, matrix form", "What interviewers probe next").
+//
+//   D_i  = sum_d dO_id O_id                      (bwd_prep_kernel)
+//   dP   = dO V^T,  dS = P * (dP - D_i)          (the softmax Jacobian)
+//   dQ   = scale dS K                             (bwd_dq_kernel: query tiles)
+//   dV   = P^T dO                                  (bwd_dkdv_kernel<false>: key tiles)
+//   dK   = scale dS^T Q                            (bwd_dkdv_kernel<true>: key tiles)
+//
+// Each kernel recomputes the scores (and dP where it needs it) over the tiles
+// it owns, so every gradient row is summed inside one workgroup (no atomics,
+// deterministic).
+//
+// bwd_dq_kernel keeps the forward's layout: each wave owns 32 queries (the
+// lane's column of every accumulator), Q and dO rows live in VGPRs as MFMA B
+// operands, K and V blocks of 64 keys stream through LDS (buffer loads
+// straight to LDS, double buffered), S^T = K Q^T and dP^T = V dO^T are MFMA
+// contractions whose accumulators hold 8 consecutive keys per 8 registers,
+// so the bf16 dS^T is directly the B operand of dQ^T += K^T dS^T (K read
+// transposed from LDS).
+//
+// bwd_dkdv_kernel swaps the roles: each wave owns 32 keys (V rows in VGPRs
+// for dK), the tile's 128 K rows stay in LDS, and blocks of 32 queries (Q,
+// dO, and their LSE and D) stream through LDS.  S = Q K^T and dP = dO V^T
+// hold, per lane, 8 consecutive queries per 8 registers, which makes the
+// bf16 P and dS the B operands of dV^T += dO^T P and dK^T += Q^T dS (dO and
+// Q read transposed).
+#include "device_common.h"
+#include "launch.h"
+#include "tile_layout.h"
+
+namespace osfa {
+namespace {
+
+constexpr int D = 128;
+constexpr int kW = 4;                 // waves per workgroup
+constexpr int kT = 64 * kW;           // threads per workgroup
+constexpr int kTile = 32 * kW;        // queries (dq) or keys (dkdv) per workgroup
+constexpr int kQb = 32;               // queries per block in bwd_dkdv_kernel
+constexpr int NKK = D / 16;
+constexpr int NMD = D / 32;
+
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  const float* lse;
+  float* delta;  // workspace [B, H, N]: D_i
+  float* lse2;   // workspace [B, H, N]: LSE_i log2(e), +inf for a row with no key
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  const int32_t* kv_len;
+  int B, H, N;
+  float c;      // scale * log2(e)
+  float scale;
+  int causal, window;
+  int n_tiles;  // ceil(N / kTile)
+  int total;    // B * H * n_tiles
+};
+
+// Workgroups go to the 8 XCDs round-robin; each XCD takes a contiguous range
+// of logical tiles (the tiles of one head share K, V, Q and dO in its L2).
+struct Tile {
+  int bh, t0;
+  bool valid;
+};
+__device__ __forceinline__ Tile map_tile(const BwdParams& p, bool ascending) {
+  const int per_xcd = gridDim.x / 8;  // grid padded to a multiple of 8
+  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  Tile t;
+  t.valid = logical < p.total;
+  t.bh = logical / p.n_tiles;
+  const int r = logical - t.bh * p.n_tiles;
+  t.t0 = (ascending ? r : p.n_tiles - 1 - r) * kTile;
+  return t;
+}
+
+__device__ __forceinline__ int key_limit(const BwdParams& p, int b) {
+  int klen = p.N;
+  if (p.kv_len) {
+    klen = p.kv_len[b];
+    klen = klen < 0 ? 0 : (klen > p.N ? p.N : klen);
+  }
+  return klen;
+}
+
+// Does some query of [qa, qb] see some key of [ja, jb]?  (j < jmax, causal
+// j <= i, window |i - j| < W.)
+__device__ __forceinline__ bool any_visible(const BwdParams& p, int jmax, int qa, int qb, int ja, int jb) {
+  if (ja >= jmax) return false;
+  if (p.causal) {
+    if (ja > qb) return false;
+    if (p.window > 0 && qa - jb >= p.window) return false;
+  } else if (p.window > 0) {
+    if (qa - jb >= p.window || ja - qb >= p.window) return false;
+  }
+  return true;
+}
+// Does every query of [qa, qb] (all < N) see every key of [ja, jb]?
+__device__ __forceinline__ bool all_visible(const BwdParams& p, int jmax, int qa, int qb, int ja, int jb) {
+  if (jb >= jmax) return false;
+  if (p.causal && jb > qa) return false;
+  if (p.window > 0) {
+    if (qb - ja >= p.window) return false;
+    if (!p.causal && jb - qa >= p.window) return false;
+  }
+  return true;
+}
+
+// Visibility of a score whose (query - key) offset is base + off, off a
+// per-register constant of either sign: lo < off <= hi.
+struct Band {
+  int lo, hi;
+};
+__device__ __forceinline__ Band band(const BwdParams& p, int base) {
+  Band b{-(1 << 30), 1 << 30};
+  if (p.causal) b.lo = max(b.lo, -base - 1);                       // i - j >= 0
+  if (p.window > 0) {
+    b.hi = min(b.hi, p.window - 1 - base);                         // i - j < W
+    if (!p.causal) b.lo = max(b.lo, -p.window - base);             // j - i < W
+  }
+  return b;
+}
+
+// Buffer loads straight to LDS of rows [r0, r0 + 4 NLD) of a [N, 128] bf16
+// matrix in the layout of tile_layout.h: load t of wave w fills 1 KB (rows
+// 4 (w + kW t) .. + 3 of the block).  Rows past N read row N - 1.
+template <int NLD>
+__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t rs, char* dst, int r0, int N, int w, int lane) {
+#pragma unroll
+  for (int t = 0; t < NLD / kW; ++t) {
+    const int row = 4 * (w + kW * t) + (lane >> 4);
+    const int grow = min(r0 + row, N - 1);
+    const int off = (grow * D + 8 * ((lane & 15) ^ swz(row))) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (w + kW * t) * 1024),
+                                             16, (int)off, 0, 0, 0);
+  }
+}
+
+// The 16-byte row fragment (chunk 2 kk + hf) of row `row` of a staged block.
+__device__ __forceinline__ bf16x8 row_frag(const char* blk, int row, int kk, int hf) {
+  return *reinterpret_cast<const bf16x8*>(blk + kv_off(row, 2 * kk + hf));
+}
+
+// Transposed reads: 8 consecutive rows (16 g + 8 hf .. + 7) of column
+// 32 md + l32 of a staged block, as the A operand of a 32x32x16 MFMA.
+struct TrOff {
+  int off[2][NMD];
+};
+__device__ __forceinline__ TrOff tr_offsets(int lane) {
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  const int rowoff = 8 * (tr_g >> 1) + (tr_j >> 2);
+  const int col = 16 * (tr_g & 1) + 4 * (tr_j & 3);
+  const int byte = (tr_j & 1) * 8;
+  TrOff t;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) t.off[r][md] = kv_off(4 * r + rowoff, (32 * md + col) >> 3) + byte;
+  return t;
+}
+__device__ __forceinline__ bf16x8 tr_frag(const char* blk, const TrOff& t, int md, int g) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x4 h[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(blk + t.off[r][md] + 4096 * g));
+  const s16x8 hv = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  return __builtin_bit_cast(bf16x8, hv);
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO_id O_id and LSE_i in log2 units (+inf for a row with no key,
+// so that exp2(s - lse2) is 0 there).  16 lanes per row, 16 rows per block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long rows) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + 8 * part);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + row * D + 8 * part);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(a[e]), bf16_lo(g[e]), acc);
+      acc = fmaf(bf16_hi(a[e]), bf16_hi(g[e]), acc);
+    }
+  }
+  // Sum over the 16 lanes of the row.
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
+  if (row < rows && part == 0) {
+    p.delta[row] = acc;
+    const float l = p.lse[row];
+    p.lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query tiles of 128, key blocks of 64.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int BLK = kBc * D * 2;  // 16 KB
+  constexpr int LOADS = 16;         // load instructions per block (1 KB each)
+  __shared__ __attribute__((aligned(1024))) char k0[BLK];
+  __shared__ __attribute__((aligned(1024))) char k1[BLK];
+  __shared__ __attribute__((aligned(1024))) char v0[BLK];
+  __shared__ __attribute__((aligned(1024))) char v1[BLK];
+
+  const Tile tile = map_tile(p, false);
+  if (!tile.valid) return;
+  const int b = tile.bh / p.H;
+  const int q0 = tile.t0;
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)tile.bh * N;
+  const int jmax = key_limit(p, b);
+
+  // Key range of the tile (as the forward).
+  int kend = jmax;
+  if (p.causal) kend = min(kend, q0 + kTile);
+  if (p.window > 0 && !p.causal) kend = min(kend, q0 + kTile - 1 + p.window);
+  const int kbeg = p.window > 0 ? max(0, q0 - p.window + 1) : 0;
+  const int kb_lo = kbeg / kBc;
+  const int nblk = kend > kbeg ? (kend + kBc - 1) / kBc - kb_lo : 0;
+
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * D), 0, N * D * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head * D), 0, N * D * 2, kBufDword3);
+  auto load_block = [&](int j, char* kd, char* vd) {
+    stage_rows<LOADS>(krs, kd, (kb_lo + j) * kBc, N, w, lane);
+    stage_rows<LOADS>(vrs, vd, (kb_lo + j) * kBc, N, w, lane);
+  };
+  if (nblk > 0) load_block(0, k0, v0);
+
+  const int qi = q0 + 32 * w + l32;
+  const bool qok = qi < N;
+  bf16x8 qreg[NKK], doreg[NKK];
+  {
+    const size_t r = head + (size_t)(qok ? qi : 0);
+    const u32x4* qs = reinterpret_cast<const u32x4*>(p.q + r * D + 8 * hf);
+    const u32x4* gs = reinterpret_cast<const u32x4*>(p.dout + r * D + 8 * hf);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qreg[kk] = __builtin_bit_cast(bf16x8, qok ? qs[2 * kk] : u32x4{0, 0, 0, 0});
+      doreg[kk] = __builtin_bit_cast(bf16x8, qok ? gs[2 * kk] : u32x4{0, 0, 0, 0});
+    }
+  }
+  const float lse2 = qok ? p.lse2[head + qi] : __builtin_huge_valf();
+  const float dlt = qok ? p.delta[head + qi] : 0.0f;
+  const float c = p.c;
+  const int qa = q0 + 32 * w, qb = qa + 31;
+  const int krow = perm_key(l32);
+  const TrOff tro = tr_offsets(lane);
+
+  f32x16 acc[NMD];
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[md][r] = 0.0f;
+
+  auto block = [&](int j, const char* kl, const char* vl) {
+    const int j0 = (kb_lo + j) * kBc;
+    if (!any_visible(p, jmax, qa, qb, j0, j0 + kBc - 1)) return;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kt][r] = 0.0f;
+        dp[kt][r] = 0.0f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(kl, 32 * kt + krow, kk, hf), qreg[kk], s[kt], 0, 0, 0);
+        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(vl, 32 * kt + krow, kk, hf), doreg[kk], dp[kt], 0, 0, 0);
+      }
+    }
+    // Register r of group kt holds key j0 + 32 kt + 16 (r / 8) + 8 hf + r % 8
+    // of query qi: masked scores take P = 0, and so dS = 0.
+    const bool full = all_visible(p, jmax, qa, qb, j0, j0 + kBc - 1);
+    const Band bd = band(p, qi - j0 - 8 * hf);
+    const int jlim = jmax - j0 - 8 * hf;  // key offset limit (padding and N)
+    bf16x8 ds[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * t + e;
+          const int off = 32 * kt + 16 * t + e;  // key offset minus 8 hf
+          // i - j = (qi - j0 - 8 hf) + (-off).
+          float x = s[kt][r];
+          if (!full) {
+            const bool vis = (off < jlim) & (-off > bd.lo) & (-off <= bd.hi);
+            x = vis ? x : kNegInf;
+          }
+          const float pr = fast_exp2(fmaf(x, c, -lse2));
+          f[e] = pr * (dp[kt][r] - dlt);
+        }
+        ds[kt][t] = __builtin_convertvector(f, bf16x8);
+      }
+    // dQ^T += K^T dS^T: K read transposed, 16 keys per MFMA.
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(kl, tro, md, g), ds[g >> 1][g & 1], acc[md], 0, 0, 0);
+  };
+
+  for (int j = 0; j < nblk; ++j) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    const bool odd = j & 1;
+    if (j + 1 < nblk) {
+      if (odd)
+        load_block(j + 1, k0, v0);
+      else
+        load_block(j + 1, k1, v1);
+    }
+    if (odd)
+      block(j, k1, v1);
+    else
+      block(j, k0, v0);
+  }
+
+  if (qok) {
+    __bf16* dst = p.dq + (head + qi) * D;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 wv;
+        wv[0] = pack_bf16x2(acc[md][4 * rq + 0] * p.scale, acc[md][4 * rq + 1] * p.scale);
+        wv[1] = pack_bf16x2(acc[md][4 * rq + 2] * p.scale, acc[md][4 * rq + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(dst + 32 * md + 8 * rq + 4 * hf) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK (DK) or dV (!DK): key tiles of 128, query blocks of 32.  The two
+// gradients are separate launches: one accumulator of 32 keys x 128 columns
+// per wave (64 VGPRs) leaves room for two waves per SIMD, where both (128
+// VGPRs) would not; the scores are recomputed by each.
+// ---------------------------------------------------------------------------
+template <bool DK>
+__global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int QBLK = kQb * D * 2;  // 8 KB
+  __shared__ __attribute__((aligned(1024))) char ktile[kTile * D * 2];  // 32 KB
+  __shared__ __attribute__((aligned(1024))) char q0b[QBLK];
+  __shared__ __attribute__((aligned(1024))) char q1b[QBLK];
+  __shared__ __attribute__((aligned(1024))) char g0b[QBLK];
+  __shared__ __attribute__((aligned(1024))) char g1b[QBLK];
+  __shared__ __attribute__((aligned(256))) float st0[2 * 64];  // lse2, delta of a block (+ slack)
+  __shared__ __attribute__((aligned(256))) float st1[2 * 64];
+
+  const Tile tile = map_tile(p, true);
+  if (!tile.valid) return;
+  const int b = tile.bh / p.H;
+  const int k0 = tile.t0;
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)tile.bh * N;
+  const int jmax = key_limit(p, b);
+
+  // Queries that can see a key of [k0, k0 + kTile).
+  int qbeg = 0, qend = N;
+  if (p.causal) qbeg = k0;
+  if (p.window > 0) {
+    qbeg = max(qbeg, k0 - p.window + 1);
+    qend = min(qend, k0 + kTile - 1 + p.window);
+  }
+  if (k0 >= jmax) qend = qbeg;  // every key of the tile is padding
+  const int qb_lo = qbeg / kQb;
+  const int nblk = qend > qbeg ? (qend + kQb - 1) / kQb - qb_lo : 0;
+
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + head * D), 0, N * D * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * D), 0, N * D * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse2 + head), 0, N * 4, kBufDword3);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.delta + head), 0, N * 4, kBufDword3);
+  auto load_block = [&](int j, char* qd, char* gd, float* sd) {
+    const int r0 = (qb_lo + j) * kQb;
+    stage_rows<8>(qrs, qd, r0, N, w, lane);
+    stage_rows<8>(grs, gd, r0, N, w, lane);
+    if (w == 0) {
+      // 64 floats from row r0 (the block's 32 and the next 32, unused);
+      // rows past N read as 0 (buffer range check).
+      // (The row offset goes in the per-lane offset, which the buffer's
+      // range check covers.)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)sd, 4, (r0 + lane) * 4, 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(sd + 64), 4,
+                                               (r0 + lane) * 4, 0, 0, 0);
+    }
+  };
+  {
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * D), 0, N * D * 2, kBufDword3);
+    stage_rows<32>(krs, ktile, k0, N, w, lane);
+  }
+  if (nblk > 0) load_block(0, q0b, g0b, st0);
+
+  // V rows of this wave's keys as B operands of dP (rows past N read as 0).
+  const int kj = k0 + 32 * w + l32;
+  bf16x8 vreg[NKK];
+  if constexpr (DK) {
+    const bool ok = kj < N;
+    const u32x4* vs = reinterpret_cast<const u32x4*>(p.v + (head + (ok ? kj : 0)) * D + 8 * hf);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) vreg[kk] = __builtin_bit_cast(bf16x8, ok ? vs[2 * kk] : u32x4{0, 0, 0, 0});
+  }
+  const float c = p.c;
+  const int ja = k0 + 32 * w, jb = ja + 31;
+  const int qrow = perm_key(l32);
+  const TrOff tro = tr_offsets(lane);
+
+  f32x16 acc[NMD];  // dK^T or dV^T
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[md][r] = 0.0f;
+
+  auto block = [&](int j, const char* ql, const char* gl, const float* sl) {
+    const int i0 = (qb_lo + j) * kQb;
+    if (!any_visible(p, jmax, i0, i0 + kQb - 1, ja, jb)) return;
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.0f;
+      dp[r] = 0.0f;
+    }
+    // Fragments are read one k-step ahead of their MFMAs (sched_barrier keeps
+    // the compiler from hoisting every read, which would not fit in VGPRs).
+    bf16x8 kf = row_frag(ktile, 32 * w + l32, 0, hf), qf = row_frag(ql, qrow, 0, hf), gf = kf;
+    if constexpr (DK) gf = row_frag(gl, qrow, 0, hf);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8 kn = kf, qn = qf, gn = gf;
+      if (kk + 1 < NKK) {
+        kn = row_frag(ktile, 32 * w + l32, kk + 1, hf);
+        qn = row_frag(ql, qrow, kk + 1, hf);
+        if constexpr (DK) gn = row_frag(gl, qrow, kk + 1, hf);
+      }
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf, s, 0, 0, 0);
+      if constexpr (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, vreg[kk], dp, 0, 0, 0);
+      kf = kn;
+      qf = qn;
+      gf = gn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Register r holds query i0 + 16 (r / 8) + 8 hf + r % 8 of key kj.
+    const bool full = (i0 + kQb <= N) && all_visible(p, jmax, i0, i0 + kQb - 1, ja, jb);
+    const Band bd = band(p, i0 + 8 * hf - kj);   // i - j = base + off
+    const bool kvis = kj < jmax;
+    const int ilim = N - i0 - 8 * hf;            // query offset limit
+    // B operands: P (for dV) or dS = P (dP - D) (for dK), bf16.
+    bf16x8 pb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(sl + 16 * t + 8 * hf);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(sl + 16 * t + 8 * hf + 4);
+      f32x4 d0, d1;
+      if constexpr (DK) {
+        d0 = *reinterpret_cast<const f32x4*>(sl + 64 + 16 * t + 8 * hf);
+        d1 = *reinterpret_cast<const f32x4*>(sl + 64 + 16 * t + 8 * hf + 4);
+      }
+      f32x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t + e;
+        const int off = 16 * t + e;
+        const float l2 = e < 4 ? l0[e] : l1[e - 4];
+        float x = s[r];
+        if (!full) {
+          const bool vis = kvis & (off < ilim) & (off > bd.lo) & (off <= bd.hi);
+          x = vis ? x : kNegInf;
+        }
+        const float pr = fast_exp2(fmaf(x, c, -l2));
+        if constexpr (DK) {
+          const float dl = e < 4 ? d0[e] : d1[e - 4];
+          f[e] = pr * (dp[r] - dl);
+        } else {
+          f[e] = pr;
+        }
+      }
+      pb[t] = __builtin_convertvector(f, bf16x8);
+    }
+    // dV^T += dO^T P or dK^T += Q^T dS, 16 queries per MFMA; the transposed
+    // fragments are read one step ahead.
+    const char* tl = DK ? ql : gl;
+    bf16x8 fa = tr_frag(tl, tro, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NMD; ++i) {
+      const int md = i >> 1, t = i & 1;
+      bf16x8 fn = fa;
+      if (i + 1 < 2 * NMD) fn = tr_frag(tl, tro, (i + 1) >> 1, (i + 1) & 1);
+      acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, pb[t], acc[md], 0, 0, 0);
+      fa = fn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int j = 0; j < nblk; ++j) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    const bool odd = j & 1;
+    if (j + 1 < nblk) {
+      if (odd)
+        load_block(j + 1, q0b, g0b, st0);
+      else
+        load_block(j + 1, q1b, g1b, st1);
+    }
+    if (odd)
+      block(j, q1b, g1b, st1);
+    else
+      block(j, q0b, g0b, st0);
+  }
+  // With no query block the K tile's loads were never waited for; no load
+  // into LDS may still be in flight when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  if (kj < N) {
+    __bf16* dst = (DK ? p.dk : p.dv) + (head + kj) * D;
+    const float f = DK ? p.scale : 1.0f;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 wv;
+        wv[0] = pack_bf16x2(acc[md][4 * rq + 0] * f, acc[md][4 * rq + 1] * f);
+        wv[1] = pack_bf16x2(acc[md][4 * rq + 2] * f, acc[md][4 * rq + 3] * f);
+        *reinterpret_cast<u32x2*>(dst + 32 * md + 8 * rq + 4 * hf) = wv;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const __bf16*>(a.q);
+  p.k = static_cast<const __bf16*>(a.k);
+  p.v = static_cast<const __bf16*>(a.v);
+  p.o = static_cast<const __bf16*>(a.o);
+  p.dout = static_cast<const __bf16*>(a.dout);
+  p.lse = a.lse;
+  const size_t rows = (size_t)a.B * a.H * a.N;
+  p.delta = a.ws;
+  p.lse2 = a.ws + rows;
+  p.dq = static_cast<__bf16*>(a.dq);
+  p.dk = static_cast<__bf16*>(a.dk);
+  p.dv = static_cast<__bf16*>(a.dv);
+  p.kv_len = a.kv_len;
+  p.B = a.B;
+  p.H = a.H;
+  p.N = a.N;
+  p.scale = a.scale;
+  p.c = a.scale * kLog2e;
+  p.causal = a.causal;
+  // |i - j| <= N - 1 always, so a window beyond N masks nothing; clamping it
+  // keeps every bound below int range.
+  p.window = a.window > a.N ? a.N : a.window;
+  p.n_tiles = (a.N + kTile - 1) / kTile;
+  p.total = a.B * a.H * p.n_tiles;
+  const unsigned grid = (unsigned)((p.total + 7) / 8 * 8);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, (long long)rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(grid), dim3(kT), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(grid), dim3(kT), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace osfa

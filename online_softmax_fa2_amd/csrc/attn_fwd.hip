@@ -38,16 +38,14 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "tile_layout.h"
 
 namespace osfa {
 namespace {
 
-constexpr int kBc = 64;           // keys per block
 constexpr int kWaves = 4;         // waves per workgroup
 constexpr int kBr = 32 * kWaves;  // queries per tile
 constexpr int kThreads = 64 * kWaves;
-// s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima.
-constexpr int kWaitVmcnt0 = 0x0F70;
 // Lazy rescale: the reference m_ref of l and A moves only when a block's row
 // maximum exceeds it by more than kTau (log2 units), so P = exp2(s - m_ref)
 // stays <= 2^kTau.  Exact: O = A / l and LSE = m_ref + log2 l do not depend on
@@ -158,10 +156,6 @@ __device__ __forceinline__ bool rows_see_all(const FwdParams& p, int jmax, int q
   return true;
 }
 
-// Row m of the S^T MFMA takes key perm_key(m) of the 32-key group: bits 2 and
-// 3 swapped.  With the 32x32 accumulator layout (lane l, register r holds row
-// 8(r/4) + 4(l/32) + r%4) this puts keys 16(r/8) + 8(l/32) + r%8 in register r.
-__device__ __forceinline__ int perm_key(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // ---------------------------------------------------------------------------
 // bf16 inputs, MFMA 32x32x16
@@ -400,19 +394,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 // bf16 inputs, d = 128: direct-to-LDS loads, swizzled LDS, transposed V
 // reads, software pipelined across key blocks
 //
-// K and V blocks (64 keys x 256 B each) are copied from global memory into
-// LDS by buffer_load ... lds (16 B per lane, no VGPR staging), one barrier
-// per block.  Each load instruction fills 1 KB of LDS = 4 key rows in lane
-// order; the lane fetches whichever 16-byte chunk belongs at its LDS slot
-// under the layout
-//     byte(row, chunk) = row * 256 + ((chunk ^ f(row)) * 16),
-//     f(row) = ((row & 3) << 2) | ((row >> 2) & 3),
-// an XOR swizzle under which the K-fragment reads (32 rows, one chunk) and
-// the V^T transposed reads (8 rows x 64 B) both touch every LDS bank once.
-// V stays row-major in LDS; ds_read_b64_tr_b16 returns, in each group of 16
-// lanes, lane i's 4 values from the 4 chunks addressed by lanes 4e + i/4,
-// element i % 4, so that a lane receives 4 consecutive keys of one d column:
-// two such reads form the 8-key A operand of the P V MFMA.
+// K and V blocks (64 keys x 256 B each) are copied into LDS by buffer loads
+// straight to LDS in the swizzled layout of tile_layout.h, one barrier per
+// block.  K fragments are row reads; V stays row-major in LDS and is read
+// transposed (ds_read_b64_tr_b16), two reads forming the 8-key A operand of
+// the P V MFMA.
 //
 // One wave's work on consecutive key blocks is overlapped so that the
 // exponentials run while the matrix core is busy:
@@ -431,11 +417,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 // V_{j+1}.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int kv_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
 
-// Word 3 of a raw buffer resource (gfx9 family: 32-bit data format).
-constexpr int kBufDword3 = 0x00020000;
 // LDS fragment reads are issued this many MFMA slots ahead of their use.
 constexpr int KAHEAD = 4, VAHEAD = 4;
 
@@ -1080,7 +1062,9 @@ FwdParams make_params(const FwdArgs& a, int br) {
   p.N = a.N;
   p.c = a.scale * kLog2e;
   p.causal = a.causal ? 1 : 0;
-  p.window = a.window > 0 ? a.window : 0;
+  // |i - j| <= N - 1 always, so a window beyond N masks nothing; clamping it
+  // keeps every bound below int range.
+  p.window = a.window > 0 ? (a.window > a.N ? a.N : a.window) : 0;
   p.br = br;
   p.n_tiles = (a.N + br - 1) / br;
   p.total = a.B * a.H * p.n_tiles;

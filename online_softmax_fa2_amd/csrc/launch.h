@@ -24,6 +24,24 @@ struct FwdArgs {
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* kv_len;  // device [B] or nullptr
+  float* ws;              // [2, B, H, N]: D and LSE in log2 units
+  int B, H, N, d;
+  float scale;
+  int causal, window;
+};
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* k;

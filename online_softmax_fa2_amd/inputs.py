@@ -11,6 +11,8 @@ Recipe (every draw is reproducible from the seed list alone):
     draws Q, K, V in that order with ``standard_normal(dtype=float32)``;
   * extra draws (the key subset that is scaled by 8) use
     ``default_rng([seed, 1000])``;
+  * the incoming gradient dO of the backward pass: for each (b, h) slice,
+    ``default_rng([seed, 2000, b, h])`` draws ``standard_normal(float32)``;
   * row softmax: ``default_rng([seed, r // 256])`` draws blocks of 256 rows of
     ``standard_normal(float32)`` which are multiplied by the workload's sigma
     (4, a power of two, so the product is exact).
@@ -114,6 +116,15 @@ def attn_inputs(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", seed: in
     if kv_len is not None:
         out.kv_len = np.asarray(kv_len, dtype=np.int32).reshape(B)
     return out
+
+
+def grad_inputs(B: int, H: int, N: int, d: int, *, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """dO [B, H, N, d] from N(0, 1) per (b, h) slice, rounded to bfloat16: (bits, float32 values)."""
+    do = np.empty((B, H, N, d), np.float32)
+    for b in range(B):
+        for h in range(H):
+            do[b, h] = np.random.default_rng([seed, 2000, b, h]).standard_normal((N, d), dtype=np.float32)
+    return bf16_round(do)
 
 
 def decode_inputs(B: int, H: int, Nkv: int, d: int, *, seed: int = 0, dtype: str = "bf16"):

@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("attn_fwd", "attn_decode_splitkv", "attn_decode_splitkv_workspace_bytes",
+    for want in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_splitkv",
+                 "attn_decode_splitkv_workspace_bytes",
                  "online_softmax_rows", "online_softmax_topk_rows", "attn_last_error", "osfa_version"):
         assert want in names
 
@@ -112,6 +113,40 @@ def _dec(lib, **kw):
 def test_decode_rejects(lib, kw, status, msg):
     assert _dec(lib, **kw) == status
     assert msg in lib.attn_last_error().decode()
+
+
+def _bwd(lib, **kw):
+    a = dict(dtype=bd.ATTN_BF16, Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, B=1, H=2,
+             N=16, d=128, scale=0.1, causal=0, window=0, kv_len=None, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.attn_bwd(a["dtype"], a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"],
+                        a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["window"], a["kv_len"], a["ws"],
+                        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dO=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(ws=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(N=0), bd.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(d=64), bd.ATTN_ERR_UNSUPPORTED, "not built"),
+    (dict(dtype=bd.ATTN_F32), bd.ATTN_ERR_UNSUPPORTED, "bf16"),
+    (dict(dtype=5), bd.ATTN_ERR_INVALID_ARG, "dtype"),
+    (dict(scale=0.0), bd.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(causal=2), bd.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(window=-3), bd.ATTN_ERR_INVALID_ARG, "window"),
+    (dict(ws_bytes=2 * 2 * 16 * 4 - 1), bd.ATTN_ERR_INVALID_ARG, "workspace"),
+    (dict(dK=FAKE + 8), bd.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(LSE=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(N=1 << 23), bd.ATTN_ERR_INVALID_ARG, "one head"),
+])
+def test_bwd_rejects(lib, kw, status, msg):
+    assert _bwd(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 2 * 2 * 3 * 5 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 3, 5) == 0
 
 
 @pytest.mark.parametrize("args,msg", [

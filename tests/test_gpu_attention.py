@@ -71,6 +71,8 @@ CASES = [
     (1, 1, 256, 64, True, 64, [100], 0),          # window + padding: rows 163.. see nothing
     (1, 3, 513, 128, False, 0, [257], 4),
     (3, 2, 127, 128, False, 1000, None, 0),
+    (1, 1, 200, 64, False, 2**31 - 1, None, 0),   # window beyond N: no mask
+    (2, 1, 150, 128, True, 2**31 - 1, [150, 77], 0),
 ]
 
 
