@@ -5,7 +5,10 @@ One step runs every kernel of the path once, each on its own workload:
     last 512 keys padded, 1 % of keys scaled by 8  (the headline workload);
   * attn_decode_splitkv, bf16, 32 heads, 131072 keys, d=128, 64 splits;
   * online_softmax_rows, float32, 4096 x 4000;
-  * online_softmax_topk_rows, float32, 1024 x 25000, k=5.
+  * online_softmax_topk_rows, float32, 1024 x 25000, k=5;
+  * attn_bwd (not part of `value`): the backward pass of the headline
+    workload for a seeded dO, from the O and LSE the forward wrote, counted
+    at 10 d FLOPs per visible query-key pair.
 Inputs are seeded synthetic data already resident in HBM.  Each kernel is
 bracketed by HIP events on the stream it is launched on; `value` is the
 forward pass's algorithmic TFLOP/s (4 d FLOPs per visible query-key pair)
@@ -62,7 +65,8 @@ def main():
 
     import online_softmax_fa2_amd as osfa
     from online_softmax_fa2_amd import accounting as acc
-    from online_softmax_fa2_amd.inputs import WORKLOADS, decode_slice, softmax_rows_inputs, workload_attn_inputs
+    from online_softmax_fa2_amd.inputs import (WORKLOADS, decode_slice, grad_inputs, softmax_rows_inputs,
+                                              workload_attn_inputs)
 
     osfa.load_library()  # raises if the HIP library is missing
     dev = torch.device("cuda:0")
@@ -80,6 +84,11 @@ def main():
     flse = torch.empty((fw["B"], fw["H"], fw["N"]), dtype=torch.float32, device=dev)
     fkv = torch.from_numpy(fin.kv_len).to(dev)
     fw_flops = acc.attn_flops(fw["B"], fw["H"], fw["N"], fw["d"], fw["causal"], fw["window"], fin.kv_len)
+    # backward of the same workload
+    bdo = up_bf16(grad_inputs(fw["B"], fw["H"], fw["N"], fw["d"], seed=fw["seed"])[0])
+    bdq, bdk, bdv = torch.empty_like(fq), torch.empty_like(fq), torch.empty_like(fq)
+    bws = torch.empty(osfa.bwd_workspace_bytes(fw["B"], fw["H"], fw["N"]) // 4, dtype=torch.float32, device=dev)
+    bw_flops = acc.attn_bwd_flops(fw["B"], fw["H"], fw["N"], fw["d"], fw["causal"], fw["window"], fin.kv_len)
 
     # --- decode workload --------------------------------------------------------
     dw_name = "decode_bf16_b1h32_nkv131072_d128_split64"
@@ -129,6 +138,11 @@ def main():
         ("online_softmax_topk_rows", lambda: check(lib.online_softmax_topk_rows(tx.data_ptr(), None, tv.data_ptr(),
                                                                                 ti.data_ptr(), tw["rows"],
                                                                                 tw["cols"], tw["k"], sh))),
+        ("attn_bwd", lambda: check(lib.attn_bwd(1, fq.data_ptr(), fk.data_ptr(), fv.data_ptr(), fo.data_ptr(),
+                                                bdo.data_ptr(), flse.data_ptr(), bdq.data_ptr(), bdk.data_ptr(),
+                                                bdv.data_ptr(), fw["B"], fw["H"], fw["N"], fw["d"], fin.scale, 1,
+                                                fw["window"], fkv.data_ptr(), bws.data_ptr(), bws.numel() * 4,
+                                                sh))),
     ]
 
     def step(events=None):
@@ -163,6 +177,7 @@ def main():
     sm_gbs = sm_bytes / (ms["online_softmax_rows"] * 1e-3) / 1e9
     tk_bytes = acc.topk_bytes(tw["rows"], tw["cols"], tw["k"])
     tk_gbs = tk_bytes / (ms["online_softmax_topk_rows"] * 1e-3) / 1e9
+    bwd_tflops = bw_flops / (ms["attn_bwd"] * 1e-3) / 1e12
 
     cpu = cpu_baseline(fin, fw, args.cpu_seconds)
 
@@ -213,6 +228,10 @@ def main():
                                          "min_us": round(ms_min["online_softmax_topk_rows"] * 1e3, 2),
                                          "gbs": round(tk_gbs, 1),
                                          "frac_hbm_peak": round(tk_gbs / acc.PEAK_HBM_GBS, 4), "bytes": tk_bytes},
+            "attn_bwd": {"workload": fw_name, "avg_us": round(ms["attn_bwd"] * 1e3, 2),
+                         "min_us": round(ms_min["attn_bwd"] * 1e3, 2), "tflops": round(bwd_tflops, 2),
+                         "frac_mfma_peak": round(bwd_tflops / acc.PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_flop": bw_flops},
         },
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1),

@@ -37,6 +37,14 @@ def attn_flops(B: int, H: int, N: int, d: int, causal: bool, window: int, kv_len
     return 4.0 * d * H * total
 
 
+def attn_bwd_flops(B: int, H: int, N: int, d: int, causal: bool, window: int, kv_len=None) -> float:
+    """Five d-long products per visible pair (S, dP, dV, dQ, dK): 10 d FLOPs, 2.5x the forward.
+
+    The recomputation of S and dP that a split backward makes is not counted.
+    """
+    return 2.5 * attn_flops(B, H, N, d, causal, window, kv_len)
+
+
 def decode_bytes(B: int, H: int, Nkv: int, d: int, elem: int = 2) -> int:
     """K and V read once (the q read and the float32 o write are < 0.01 % and not counted)."""
     return 2 * B * H * Nkv * d * elem
