@@ -13,6 +13,10 @@ Recipe (every draw is reproducible from the seed list alone):
     ``default_rng([seed, 1000])``;
   * the incoming gradient dO of the backward pass: for each (b, h) slice,
     ``default_rng([seed, 2000, b, h])`` draws ``standard_normal(float32)``;
+  * FP8 attention: the float32 Q, K, V of the attention recipe (big keys
+    included), each tensor divided by its descale max|x| / 448 (float32,
+    nudged up until no quotient exceeds 448) and rounded to e4m3 (OCP e4m3fn,
+    round to nearest even); the oracle sees code x descale in float64;
   * row softmax: ``default_rng([seed, r // 256])`` draws blocks of 256 rows of
     ``standard_normal(float32)`` which are multiplied by the workload's sigma
     (4, a power of two, so the product is exact).
@@ -41,6 +45,40 @@ def bf16_round(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     bits = ((u + bias) >> 16).astype(np.uint16)
     values = (bits.astype(np.uint32) << 16).view(np.float32)
     return bits, values
+
+
+def e4m3_round(y: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Round finite values with |y| <= 448 to OCP e4m3fn, ties to even: (codes uint8, values float64).
+
+    e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits; subnormals below
+    2^-6 in steps of 2^-9; 448 is the largest finite value (0x7E).
+    """
+    y = np.asarray(y, np.float64)
+    if not np.all(np.isfinite(y)) or np.abs(y).max(initial=0.0) > 448.0:
+        raise ValueError("e4m3_round: values must be finite with |y| <= 448")
+    a = np.abs(y)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    quantum = np.exp2(e - 3.0)
+    q = np.rint(a / quantum) * quantum  # exact division by a power of two; rint ties to even
+    E = np.floor(np.log2(np.where(q > 0, q, 1.0)))
+    sub = q < 2.0 ** -6
+    mant = np.where(sub, q / 2.0 ** -9, q / np.exp2(E) * 8.0 - 8.0)
+    field = np.where(sub, 0.0, E + 7.0)
+    codes = (np.where(y < 0, 128, 0) + field.astype(np.int64) * 8 + mant.astype(np.int64)).astype(np.uint8)
+    codes = np.where(q == 0, 0, codes).astype(np.uint8)
+    return codes, np.where(y < 0, -q, q)
+
+
+def e4m3_descale(x: np.ndarray) -> float:
+    """float32 d with |x| / d <= 448 for every element (d = max|x| / 448, nudged up)."""
+    amax = float(np.abs(np.asarray(x, np.float64)).max(initial=0.0))
+    if amax == 0.0:
+        return 1.0
+    d = np.float32(amax / 448.0)
+    while amax / float(d) > 448.0:
+        d = np.nextafter(d, np.float32(np.inf))
+    return float(d)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -116,6 +154,39 @@ def attn_inputs(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", seed: in
     if kv_len is not None:
         out.kv_len = np.asarray(kv_len, dtype=np.int32).reshape(B)
     return out
+
+
+@dataclass
+class Fp8AttnInputs:
+    """e4m3 codes of Q, K, V with their float32 descales, and the dequantized values (float64)."""
+
+    q8: np.ndarray  # [B, H, N, d] uint8
+    k8: np.ndarray
+    v8: np.ndarray
+    qd: float
+    kd: float
+    vd: float
+    q: np.ndarray  # code value x descale, float64 (exact)
+    k: np.ndarray
+    v: np.ndarray
+    scale: float
+    causal: bool = False
+    window: int = 0
+    kv_len: np.ndarray | None = None
+
+
+def attn_fp8_inputs(B: int, H: int, N: int, d: int, *, seed: int = 0, causal: bool = False, window: int = 0,
+                    kv_len=None, n_big_keys: int = 0) -> Fp8AttnInputs:
+    """The float32 attention recipe (same draws as ``attn_inputs``), quantized per tensor to e4m3."""
+    src = attn_inputs(B, H, N, d, dtype="f32", seed=seed, causal=causal, window=window, kv_len=kv_len,
+                      n_big_keys=n_big_keys)
+    out = {}
+    for name in ("q", "k", "v"):
+        x = getattr(src, name)
+        dsc = e4m3_descale(x)
+        codes, vals = e4m3_round(x.astype(np.float64) / dsc)
+        out[name + "8"], out[name + "d"], out[name] = codes, dsc, vals * dsc
+    return Fp8AttnInputs(scale=src.scale, causal=causal, window=window, kv_len=src.kv_len, **out)
 
 
 def grad_inputs(B: int, H: int, N: int, d: int, *, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:

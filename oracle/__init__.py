@@ -11,6 +11,8 @@ Modules
   backward  -- the gradients dQ, dK, dV of masked softmax attention, and a
                first-order bound on their rounding error (a tolerance).
   softmax   -- the direct definition of row softmax and its top-k.
+  quantized -- the error model of FP8 (e4m3) attention against the exact
+               attention of the dequantized inputs (a tolerance).
   models    -- the pages' streaming algorithms (per-element (m, d) update,
                the associative merge, the single-query and query-tile
                blockwise recurrences, split-KV), written from their
@@ -32,4 +34,5 @@ invariants and brute force.  No function is "parity unpinned".
 
 from .attention import attention_ref, decode_ref, visible_mask, visible_count  # noqa: F401
 from .softmax import softmax_ref, topk_ref  # noqa: F401
+from .quantized import attention_fp8_error_model  # noqa: F401
 from .backward import attention_bwd_ref, attention_bwd_delta, attention_bwd_error_bound  # noqa: F401
