@@ -8,7 +8,9 @@ One step runs every kernel of the path once, each on its own workload:
   * online_softmax_topk_rows, float32, 1024 x 25000, k=5;
   * attn_bwd (not part of `value`): the backward pass of the headline
     workload for a seeded dO, from the O and LSE the forward wrote, counted
-    at 10 d FLOPs per visible query-key pair.
+    at 10 d FLOPs per visible query-key pair;
+  * attn_fwd_fp8 (not part of `value`): the headline workload with Q, K, V
+    quantized per tensor to e4m3, against the FP8 matrix-core peak.
 Inputs are seeded synthetic data already resident in HBM.  Each kernel is
 bracketed by HIP events on the stream it is launched on; `value` is the
 forward pass's algorithmic TFLOP/s (4 d FLOPs per visible query-key pair)
@@ -65,8 +67,8 @@ def main():
 
     import online_softmax_fa2_amd as osfa
     from online_softmax_fa2_amd import accounting as acc
-    from online_softmax_fa2_amd.inputs import (WORKLOADS, decode_slice, grad_inputs, softmax_rows_inputs,
-                                              workload_attn_inputs)
+    from online_softmax_fa2_amd.inputs import (WORKLOADS, attn_fp8_inputs, decode_slice, grad_inputs,
+                                              softmax_rows_inputs, workload_attn_inputs)
 
     osfa.load_library()  # raises if the HIP library is missing
     dev = torch.device("cuda:0")
@@ -89,6 +91,13 @@ def main():
     bdq, bdk, bdv = torch.empty_like(fq), torch.empty_like(fq), torch.empty_like(fq)
     bws = torch.empty(osfa.bwd_workspace_bytes(fw["B"], fw["H"], fw["N"]) // 4, dtype=torch.float32, device=dev)
     bw_flops = acc.attn_bwd_flops(fw["B"], fw["H"], fw["N"], fw["d"], fw["causal"], fw["window"], fin.kv_len)
+    # FP8 forward of the same workload
+    f8 = attn_fp8_inputs(fw["B"], fw["H"], fw["N"], fw["d"], seed=fw["seed"], causal=fw["causal"],
+                         window=fw["window"], kv_len=fw["kv_len"], n_big_keys=fw["n_big_keys"])
+    f8q, f8k, f8v = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (f8.q8, f8.k8, f8.v8))
+    del f8.q, f8.k, f8.v
+    f8o = torch.empty_like(fo)
+    f8lse = torch.empty_like(flse)
 
     # --- decode workload --------------------------------------------------------
     dw_name = "decode_bf16_b1h32_nkv131072_d128_split64"
@@ -138,6 +147,10 @@ def main():
         ("online_softmax_topk_rows", lambda: check(lib.online_softmax_topk_rows(tx.data_ptr(), None, tv.data_ptr(),
                                                                                 ti.data_ptr(), tw["rows"],
                                                                                 tw["cols"], tw["k"], sh))),
+        ("attn_fwd_fp8", lambda: check(lib.attn_fwd_fp8(f8q.data_ptr(), f8k.data_ptr(), f8v.data_ptr(),
+                                                        f8o.data_ptr(), f8lse.data_ptr(), fw["B"], fw["H"], fw["N"],
+                                                        fw["d"], f8.scale, f8.qd, f8.kd, f8.vd, 1, fw["window"],
+                                                        fkv.data_ptr(), sh))),
         ("attn_bwd", lambda: check(lib.attn_bwd(1, fq.data_ptr(), fk.data_ptr(), fv.data_ptr(), fo.data_ptr(),
                                                 bdo.data_ptr(), flse.data_ptr(), bdq.data_ptr(), bdk.data_ptr(),
                                                 bdv.data_ptr(), fw["B"], fw["H"], fw["N"], fw["d"], fin.scale, 1,
@@ -178,6 +191,7 @@ def main():
     tk_bytes = acc.topk_bytes(tw["rows"], tw["cols"], tw["k"])
     tk_gbs = tk_bytes / (ms["online_softmax_topk_rows"] * 1e-3) / 1e9
     bwd_tflops = bw_flops / (ms["attn_bwd"] * 1e-3) / 1e12
+    f8_tflops = fw_flops / (ms["attn_fwd_fp8"] * 1e-3) / 1e12
 
     cpu = cpu_baseline(fin, fw, args.cpu_seconds)
 
@@ -228,6 +242,9 @@ def main():
                                          "min_us": round(ms_min["online_softmax_topk_rows"] * 1e3, 2),
                                          "gbs": round(tk_gbs, 1),
                                          "frac_hbm_peak": round(tk_gbs / acc.PEAK_HBM_GBS, 4), "bytes": tk_bytes},
+            "attn_fwd_fp8": {"workload": fw_name + " (e4m3 Q, K, V)", "avg_us": round(ms["attn_fwd_fp8"] * 1e3, 2),
+                             "min_us": round(ms_min["attn_fwd_fp8"] * 1e3, 2), "tflops": round(f8_tflops, 2),
+                             "frac_mfma_peak": round(f8_tflops / acc.PEAK_FP8_TFLOPS, 4)},
             "attn_bwd": {"workload": fw_name, "avg_us": round(ms["attn_bwd"] * 1e3, 2),
                          "min_us": round(ms_min["attn_bwd"] * 1e3, 2), "tflops": round(bwd_tflops, 2),
                          "frac_mfma_peak": round(bwd_tflops / acc.PEAK_BF16_TFLOPS, 4),

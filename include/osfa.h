@@ -82,6 +82,34 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
                        int causal, int window, const int32_t* kv_len, hipStream_t stream);
 
 /*
+ * attn_fwd_fp8 -- attn_fwd with FP8 inputs: Q, K, V are OCP e4m3 (e4m3fn)
+ * codes, one byte per element, and each tensor has one float32 descale, so
+ * that the value of an element is code x descale.  Computes the same O and
+ * LSE as attn_fwd for the dequantized Q, K, V (same masks, guard, deferred
+ * division and LSE; pages as cited there), with both products on the FP8
+ * matrix core and float32 statistics: the FP8 step the pages name for FA3
+ * (page "Derive online softmax, prove it is exact", "What interviewers probe
+ * next"; article "Online softmax", "Trade-offs and edge cases").
+ *
+ * P is rounded to e4m3 before P V, in a per-(query, 64-key block) power-of-
+ * two frame that maps the block's largest P into (128, 256]; O divides by
+ * the sum of those rounded P, LSE uses the float32 sum.  The result differs
+ * from the exact attention of the dequantized inputs by the rounding of P
+ * (relative 2^-4 per element) and the matrix core's accumulation (about
+ * 2^-15 of the sum of |terms| per instruction).
+ *
+ * Layout: Q, K, V [B, H, N, d] bytes, d fastest; O [B, H, N, d] bf16 (round
+ * to nearest even); LSE [B, H, N] float32, natural log, as attn_fwd.  Codes
+ * 0x7F and 0xFF (NaN) are out of contract.  q_descale, k_descale,
+ * v_descale: finite and > 0.  Supported: d = 128 (others ->
+ * ATTN_ERR_UNSUPPORTED); B, H, N >= 1; B * H * N * d < 2^40; N * d < 2^30;
+ * Q, K, V, O 16-byte aligned.
+ */
+attn_status_t attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+                           int d, float scale, float q_descale, float k_descale, float v_descale, int causal,
+                           int window, const int32_t* kv_len, hipStream_t stream);
+
+/*
  * attn_bwd_workspace_bytes -- bytes of device workspace that attn_bwd needs:
  * 2 * B * H * N * 4 (per query, D = rowsum(dO * O) and LSE in log2 units,
  * float32).  Returns 0 for invalid sizes.

@@ -21,7 +21,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libosfa.so")
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "softmax.hip"]
+SOURCES = ["api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "decode.hip", "softmax.hip"]
 # Packed FP32 ops are disabled for all device code: hipcc -O3 would
 # otherwise form v_pk_* float32 instructions by itself.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

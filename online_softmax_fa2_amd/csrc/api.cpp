@@ -58,6 +58,31 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
   return hip_status(e, "attn_fwd");
 }
 
+attn_status_t attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+                           int d, float scale, float q_descale, float k_descale, float v_descale, int causal,
+                           int window, const int32_t* kv_len, hipStream_t stream) {
+  if (!Q || !K || !V || !O || !LSE) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: null tensor pointer");
+  if (B < 1 || H < 1 || N < 1 || d < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: sizes must be >= 1 (B=%d H=%d N=%d d=%d)", B, H, N, d);
+  if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: head dim d=%d not built (128)", d);
+  if ((long long)B * H * N * d >= kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: B*H*N*d too large");
+  if ((long long)B * H >= (1LL << 24)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: B*H too large");
+  if ((long long)N * d >= (1LL << 30)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: N*d must be < 2^30 (one head)");
+  const float sc[4] = {scale, q_descale, k_descale, v_descale};
+  for (float x : sc)
+    if (!std::isfinite(x) || !(x > 0.0f))
+      return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: scale and descales must be finite and > 0 (got %g)", (double)x);
+  const float qk = q_descale * k_descale;
+  if (!std::isfinite(qk) || !(qk > 0.0f) || !std::isfinite(scale * qk) || !(scale * qk > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: scale * q_descale * k_descale out of float32 range");
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: causal must be 0 or 1");
+  if (window < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: window must be >= 0 (0 = no window)");
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: Q, K, V, O must be 16-byte aligned");
+  osfa::FwdArgs a{Q, K, V, O, LSE, kv_len, B, H, N, d, scale, causal, window};
+  return hip_status(osfa::launch_attn_fwd_fp8(a, qk, v_descale, stream), "attn_fwd_fp8");
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 1 || H < 1 || N < 1) return 0;
   return 2 * (size_t)B * H * N * sizeof(float);

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_splitkv",
+    for want in ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_splitkv",
                  "attn_decode_splitkv_workspace_bytes",
                  "online_softmax_rows", "online_softmax_topk_rows", "attn_last_error", "osfa_version"):
         assert want in names
@@ -112,6 +112,32 @@ def _dec(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, status, msg):
     assert _dec(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
+def _fp8(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, B=1, H=2, N=16, d=128, scale=0.1, qd=0.01, kd=0.02, vd=0.03,
+             causal=0, window=0, kv_len=None, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_fp8(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                            a["qd"], a["kd"], a["vd"], a["causal"], a["window"], a["kv_len"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(V=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(B=0), bd.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(d=64), bd.ATTN_ERR_UNSUPPORTED, "not built"),
+    (dict(qd=0.0), bd.ATTN_ERR_INVALID_ARG, "descale"),
+    (dict(vd=float("nan")), bd.ATTN_ERR_INVALID_ARG, "descale"),
+    (dict(scale=-1.0), bd.ATTN_ERR_INVALID_ARG, "descale"),
+    (dict(qd=1e30, kd=1e30), bd.ATTN_ERR_INVALID_ARG, "range"),
+    (dict(causal=3), bd.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(window=-1), bd.ATTN_ERR_INVALID_ARG, "window"),
+    (dict(O=FAKE + 4), bd.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(N=1 << 23), bd.ATTN_ERR_INVALID_ARG, "one head"),
+])
+def test_fp8_rejects(lib, kw, status, msg):
+    assert _fp8(lib, **kw) == status
     assert msg in lib.attn_last_error().decode()
 
 
