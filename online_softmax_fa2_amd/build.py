@@ -25,6 +25,12 @@ SOURCES = ["api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "decod
 # Packed FP32 ops are disabled for all device code: hipcc -O3 would
 # otherwise form v_pk_* float32 instructions by itself.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -fno-honor-nans where maxima of scores dominate the VALU work: the kernels
+# never produce or test NaN (non-finite inputs are out of contract), and it
+# lets fmaxf chains become v_max3_f32 with no NaN-quieting copies.  Not for
+# decode.hip: there it makes the compiler keep twice the VGPRs (half the
+# occupancy of an HBM-bound kernel).
+NNAN_SOURCES = {"attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "softmax.hip"}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wno-unused-command-line-argument"]
 
@@ -39,6 +45,8 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+    if src in NNAN_SOURCES:
+        cmd.append("-fno-honor-nans")
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

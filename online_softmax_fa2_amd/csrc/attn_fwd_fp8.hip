@@ -23,8 +23,9 @@
 // queries (lane = query, as in the bf16 kernels: S^T = K Q^T, O^T += V^T
 // P^T).  K and V blocks of 64 keys x 128 B are copied to LDS by buffer loads
 // straight to LDS, double buffered, in a layout where 16-byte chunk c of row
-// r sits at r * 128 + ((c ^ (r & 7)) << 4); K is read by rows, V transposed
-// with ds_read_b64_tr_b8 (8 consecutive keys of one column per lane).
+// r sits at r * 128 + ((c ^ f8_swz(r)) << 4); K is read by rows, V
+// transposed with ds_read_b64_tr_b8 (8 consecutive keys of one column per
+// lane).
 //
 // MFMA operand layout used here (checked on the device): for
 // 32x32x64 with 8-bit operands, lane l holds 32 bytes of row (A) or column
@@ -48,7 +49,12 @@ constexpr int kBlk8 = kBc * kD8;          // 8 KB per 64-key block
 constexpr int kScale1 = 127;              // E8M0 encoding of 1.0
 constexpr uint32_t kOnes4 = 0x38383838u;  // four e4m3 1.0
 
-__device__ __forceinline__ int f8_off(int row, int chunk) { return row * kD8 + ((chunk ^ (row & 7)) << 4); }
+// Chunk slot of a 128-byte row: XOR with f(row) = ((row >> 1) & 3) << 1 |
+// (row >> 3) & 1.  With 64 four-byte banks (two rows per bank line), the
+// 16 rows of a K fragment read (16 lanes x 16 B) and the 8 rows x 2 chunks
+// of a transposed V read (32 lanes x 8 B) each touch every bank once.
+__device__ __forceinline__ int f8_swz(int row) { return (((row >> 1) & 3) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int f8_off(int row, int chunk) { return row * kD8 + ((chunk ^ f8_swz(row)) << 4); }
 
 __device__ __forceinline__ i32x8 join(u32x4 a, u32x4 b) {
   return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
@@ -63,7 +69,7 @@ __device__ __forceinline__ void stage8(__amdgpu_buffer_rsrc_t rs, char* dst, int
   for (int t = 0; t < 2; ++t) {
     const int row = 8 * (w + 4 * t) + (lane >> 3);
     const int grow = min(r0 + row, N - 1);
-    const int off = grow * kD8 + 16 * ((lane & 7) ^ (row & 7));
+    const int off = grow * kD8 + 16 * ((lane & 7) ^ f8_swz(row));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (w + 4 * t) * 1024),
                                              16, off, 0, 0, 0);
   }
@@ -167,11 +173,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_d128_kernel(FwdParams p) 
         for (int r = 0; r < 16; ++r)
           if (!visible(p, kr.jmax, qi, j0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7))) s[kt][r] = kNegInf;
     }
-    float mx = kNegInf;
+    // Lane maximum of the 32 scores: four independent v_max3 chains.
+    float m4[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& x = s[g >> 1];
+      const int o = 8 * (g & 1);
+      m4[g] = vmax3(vmax3(vmax3(x[o], x[o + 1], x[o + 2]), x[o + 3], x[o + 4]), x[o + 5], x[o + 6]);
+    }
+    const float mx = vmax3(vmax3(m4[0], m4[1], s[0][7]), vmax3(m4[2], m4[3], s[0][15]), vmax(s[1][7], s[1][15]));
     const float mblk = max_halves(mx) * c;
     const bool move = mblk > m_ref + kTau;
     if (__any(move)) {

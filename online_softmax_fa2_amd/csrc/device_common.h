@@ -48,27 +48,14 @@ __device__ __forceinline__ float swap_halves(float x) {
   return (__lane_id() < 32) ? p.hi : p.lo;
 }
 // max / sum of x over lanes l and l xor 32 (order-independent, no lane test).
-// Maxima of scores and running maxima (finite or -inf, never NaN) without
-// the NaN-quieting copies the compiler puts in front of fmaxf on values it
-// cannot prove canonical (MFMA results).
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-#else
-  return fmaxf(fmaxf(a, b), c);
-#endif
-}
-__device__ __forceinline__ float vmax(float a, float b) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-#else
-  return fmaxf(a, b);
-#endif
-}
+// Maxima of scores and running maxima (finite or -inf, never NaN).  The
+// device code is built with -fno-honor-nans, so the compiler turns fmaxf
+// chains into v_max3_f32 without NaN-quieting copies, and, unlike inline
+// assembly, it sees the reads and inserts the wait states an MFMA result
+// needs before a VALU instruction reads it.  (Translation units built
+// without that flag get the quieting copies: correct, a little slower.)
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float vmax(float a, float b) { return fmaxf(a, b); }
 __device__ __forceinline__ float max_halves(float x) {
   const HalfPair p = permlane32_pair(x);
   return vmax(p.lo, p.hi);
