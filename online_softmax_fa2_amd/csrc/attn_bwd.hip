@@ -319,21 +319,21 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
         acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(kl, tro, md, g), ds[g >> 1][g & 1], acc[md], 0, 0, 0);
   };
 
-  for (int j = 0; j < nblk; ++j) {
+  auto iter = [&](int j, const char* kl, const char* vl, char* kn, char* vn) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    const bool odd = j & 1;
-    if (j + 1 < nblk) {
-      if (odd)
-        load_block(j + 1, k0, v0);
-      else
-        load_block(j + 1, k1, v1);
-    }
-    if (odd)
-      block(j, k1, v1);
-    else
-      block(j, k0, v0);
+    if (j + 1 < nblk) load_block(j + 1, kn, vn);
+    block(j, kl, vl);
+  };
+  // Two blocks per trip, one call site per buffer: with an if/else on the
+  // parity the accumulators came out of the join in different registers
+  // and were copied every block.
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    iter(j, k0, v0, k1, v1);
+    iter(j + 1, k1, v1, k0, v0);
   }
+  if (j < nblk) iter(j, k0, v0, k1, v1);
 
   if (qok) {
     __bf16* dst = p.dq + (head + qi) * D;
@@ -513,21 +513,19 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  for (int j = 0; j < nblk; ++j) {
+  auto iter = [&](int j, const char* ql, const char* gl, const float* sl, char* qn, char* gn, float* sn) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    const bool odd = j & 1;
-    if (j + 1 < nblk) {
-      if (odd)
-        load_block(j + 1, q0b, g0b, st0);
-      else
-        load_block(j + 1, q1b, g1b, st1);
-    }
-    if (odd)
-      block(j, q1b, g1b, st1);
-    else
-      block(j, q0b, g0b, st0);
+    if (j + 1 < nblk) load_block(j + 1, qn, gn, sn);
+    block(j, ql, gl, sl);
+  };
+  // Two blocks per trip, one call site per buffer (see bwd_dq_kernel).
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    iter(j, q0b, g0b, st0, q1b, g1b, st1);
+    iter(j + 1, q1b, g1b, st1, q0b, g0b, st0);
   }
+  if (j < nblk) iter(j, q0b, g0b, st0, q1b, g1b, st1);
   // With no query block the K tile's loads were never waited for; no load
   // into LDS may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -234,21 +234,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_d128_kernel(FwdParams p) 
     lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, kScale1, 0, sb);
   };
 
-  for (int j = 0; j < nblk; ++j) {
+  // Two blocks per trip, one call site per buffer: with an if/else on the
+  // parity the accumulators came out of the join in different registers
+  // and were copied every block.
+  auto iter = [&](int j, const char* kl, const char* vl, char* kn, char* vn) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    const bool odd = j & 1;
-    if (j + 1 < nblk) {
-      if (odd)
-        load_block(j + 1, k0, v0);
-      else
-        load_block(j + 1, k1, v1);
-    }
-    if (odd)
-      block(j, k1, v1);
-    else
-      block(j, k0, v0);
+    if (j + 1 < nblk) load_block(j + 1, kn, vn);
+    block(j, kl, vl);
+  };
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    iter(j, k0, v0, k1, v1);
+    iter(j + 1, k1, v1, k0, v0);
   }
+  if (j < nblk) iter(j, k0, v0, k1, v1);
 
   // Row 0 of lacc (lane l32 of the first half, register 0) is sum(rounded P)
   // for query l32; both halves need it.
