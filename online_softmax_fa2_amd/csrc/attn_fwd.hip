@@ -435,58 +435,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
   // half that no row sees is set to -inf, and only a half that a bound cuts
   // into takes a compare and a select per score.  Query tiles start at
   // multiples of 32, so a causal diagonal or a window edge cuts into one half.
-  auto mask = [&](f32x16 (&s)[2], int j0) {
-    if (rows_see_all(p, kr.jmax, qa, qb, j0)) return;
-    int hi = kr.jmax - 1 - j0;                                 // padding: j < jmax
-    int hi_min = hi, hi_max = hi;                              // over the wave's rows
-    if (p.causal) {
-      hi = min(hi, qi - j0);                                   // j <= i
-      hi_min = min(hi_min, qa - j0);
-      hi_max = min(hi_max, qb - j0);
-    }
-    int lo = -1 - kBc, lo_min = -1 - kBc, lo_max = -1 - kBc;
-    if (p.window > 0) {
-      lo = qi - p.window - j0;                                 // i - j < window
-      lo_min = qa - p.window - j0;
-      lo_max = qb - p.window - j0;
-      if (!p.causal) {
-        hi = min(hi, qi + p.window - 1 - j0);                  // j - i < window
-        hi_min = min(hi_min, qa + p.window - 1 - j0);
-        hi_max = min(hi_max, qb + p.window - 1 - j0);
-      }
-    }
-    lo -= 8 * hf;
-    hi -= 8 * hf;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int t0 = 32 * kt, t1 = 32 * kt + 31;
-      if (hi_max < t0 || lo_min >= t1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = kNegInf;
-        continue;
-      }
-      const bool need_hi = hi_min < t1, need_lo = lo_max >= t0;
-      if (need_hi && need_lo) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + 16 * (r >> 3) + (r & 7);
-          s[kt][r] = ((t > lo) & (t <= hi)) ? s[kt][r] : kNegInf;
-        }
-      } else if (need_hi) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + 16 * (r >> 3) + (r & 7);
-          s[kt][r] = (t <= hi) ? s[kt][r] : kNegInf;
-        }
-      } else if (need_lo) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + 16 * (r >> 3) + (r & 7);
-          s[kt][r] = (t > lo) ? s[kt][r] : kNegInf;
-        }
-      }
-    }
-  };
+  auto mask = [&](f32x16 (&s)[2], int j0) { mask_block(p, kr, qi, qa, qb, hf, s, j0); };
   // Row maximum of a block and the lazy reference update (sets the pending
   // accumulator factor; l is rescaled here).
   auto update_ref = [&](const f32x16 (&s)[2]) {

@@ -166,13 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_d128_kernel(FwdParams p) 
       }
     }
     // Register r of group kt holds key j0 + 32 kt + 16 (r / 8) + 8 hf + r % 8.
-    if (!rows_see_all(p, kr.jmax, qa, qb, j0)) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!visible(p, kr.jmax, qi, j0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7))) s[kt][r] = kNegInf;
-    }
+    mask_block(p, kr, qi, qa, qb, hf, s, j0);
     // Lane maximum of the 32 scores: four independent v_max3 chains.
     float m4[4];
 #pragma unroll
