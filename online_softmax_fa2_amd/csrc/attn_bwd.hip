@@ -8,8 +8,8 @@
 //   D_i  = sum_d dO_id O_id                      (bwd_prep_kernel)
 //   dP   = dO V^T,  dS = P * (dP - D_i)          (the softmax Jacobian)
 //   dQ   = scale dS K                             (bwd_dq_kernel: query tiles)
-//   dV   = P^T dO                                  (bwd_dkdv_kernel<false>: key tiles)
-//   dK   = scale dS^T Q                            (bwd_dkdv_kernel<true>: key tiles)
+//   dV   = P^T dO                                  (bwd_dkdv_kernel: key tiles)
+//   dK   = scale dS^T Q                            (bwd_dkdv_kernel)
 //
 // Each kernel recomputes the scores (and dP where it needs it) over the tiles
 // it owns, so every gradient row is summed inside one workgroup (no atomics,
@@ -23,14 +23,16 @@
 // so the bf16 dS^T is directly the B operand of dQ^T += K^T dS^T (K read
 // transposed from LDS).
 //
-// bwd_dkdv_kernel swaps the roles: each wave owns 32 keys (V rows in VGPRs
-// for dK), the tile's 128 K rows stay in LDS, and blocks of 32 queries (Q,
-// dO, and their LSE and D) stream through LDS.  S = Q K^T and dP = dO V^T
+// bwd_dkdv_kernel swaps the roles: each wave owns 32 keys (their K rows in
+// VGPRs as the B operand of S, their V rows in LDS for dP), and blocks of 32
+// queries (Q, dO, and their LSE and D) stream through LDS; P and dS are
+// formed once for both gradients.  S = Q K^T and dP = dO V^T
 // hold, per lane, 8 consecutive queries per 8 registers, which makes the
 // bf16 P and dS the B operands of dV^T += dO^T P and dK^T += Q^T dS (dO and
 // Q read transposed).
 #include "device_common.h"
 #include "launch.h"
+#include "masks.h"
 #include "tile_layout.h"
 
 namespace osfa {
@@ -103,32 +105,6 @@ __device__ __forceinline__ bool any_visible(const BwdParams& p, int jmax, int qa
   }
   return true;
 }
-// Does every query of [qa, qb] (all < N) see every key of [ja, jb]?
-__device__ __forceinline__ bool all_visible(const BwdParams& p, int jmax, int qa, int qb, int ja, int jb) {
-  if (jb >= jmax) return false;
-  if (p.causal && jb > qa) return false;
-  if (p.window > 0) {
-    if (qb - ja >= p.window) return false;
-    if (!p.causal && jb - qa >= p.window) return false;
-  }
-  return true;
-}
-
-// Visibility of a score whose (query - key) offset is base + off, off a
-// per-register constant of either sign: lo < off <= hi.
-struct Band {
-  int lo, hi;
-};
-__device__ __forceinline__ Band band(const BwdParams& p, int base) {
-  Band b{-(1 << 30), 1 << 30};
-  if (p.causal) b.lo = max(b.lo, -base - 1);                       // i - j >= 0
-  if (p.window > 0) {
-    b.hi = min(b.hi, p.window - 1 - base);                         // i - j < W
-    if (!p.causal) b.lo = max(b.lo, -p.window - base);             // j - i < W
-  }
-  return b;
-}
-
 // Buffer loads straight to LDS of rows [r0, r0 + 4 NLD) of a [N, 128] bf16
 // matrix in the layout of tile_layout.h: load t of wave w fills 1 KB (rows
 // 4 (w + kW t) .. + 3 of the block).  Rows past N read row N - 1.
@@ -271,46 +247,40 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   auto block = [&](int j, const char* kl, const char* vl) {
     const int j0 = (kb_lo + j) * kBc;
     if (!any_visible(p, jmax, qa, qb, j0, j0 + kBc - 1)) return;
-    f32x16 s[2], dp[2];
+    f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kt][r] = 0.0f;
-        dp[kt][r] = 0.0f;
-      }
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+      for (int kk = 0; kk < NKK; ++kk)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(kl, 32 * kt + krow, kk, hf), qreg[kk], s[kt], 0, 0, 0);
-        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(vl, 32 * kt + krow, kk, hf), doreg[kk], dp[kt], 0, 0, 0);
-      }
     }
     // Register r of group kt holds key j0 + 32 kt + 16 (r / 8) + 8 hf + r % 8
-    // of query qi: masked scores take P = 0, and so dS = 0.
-    const bool full = all_visible(p, jmax, qa, qb, j0, j0 + kBc - 1);
-    const Band bd = band(p, qi - j0 - 8 * hf);
-    const int jlim = jmax - j0 - 8 * hf;  // key offset limit (padding and N)
-    bf16x8 ds[2][2];
+    // of query qi: masked scores take P = 0, and so dS = 0.  P replaces S in
+    // place; dP^T is formed one 32-key group at a time (fewer live VGPRs).
+    mask_qlane(p, jmax, qi, qa, qb, hf, s, j0);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = fast_exp2(fmaf(s[kt][r], c, -lse2));
+    bf16x8 ds[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(vl, 32 * kt + krow, kk, hf), doreg[kk], dp, 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         f32x8 f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * t + e;
-          const int off = 32 * kt + 16 * t + e;  // key offset minus 8 hf
-          // i - j = (qi - j0 - 8 hf) + (-off).
-          float x = s[kt][r];
-          if (!full) {
-            const bool vis = (off < jlim) & (-off > bd.lo) & (-off <= bd.hi);
-            x = vis ? x : kNegInf;
-          }
-          const float pr = fast_exp2(fmaf(x, c, -lse2));
-          f[e] = pr * (dp[kt][r] - dlt);
-        }
+        for (int e = 0; e < 8; ++e) f[e] = s[kt][8 * t + e] * (dp[8 * t + e] - dlt);
         ds[kt][t] = __builtin_convertvector(f, bf16x8);
       }
+    }
     // dQ^T += K^T dS^T: K read transposed, 16 keys per MFMA.
 #pragma unroll
     for (int md = 0; md < NMD; ++md)
@@ -350,21 +320,21 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK (DK) or dV (!DK): key tiles of 128, query blocks of 32.  The two
-// gradients are separate launches: one accumulator of 32 keys x 128 columns
-// per wave (64 VGPRs) leaves room for two waves per SIMD, where both (128
-// VGPRs) would not; the scores are recomputed by each.
+// dK and dV: key tiles of 128, query blocks of 32.  Both 32 keys x 128
+// columns accumulators of a wave (128 VGPRs) and its K rows (32) are held in
+// registers; the V rows, needed only as the dP operand, are read from LDS
+// (staged once) and operand fragments are read just before their MFMA, which
+// keeps the kernel at two waves per SIMD.
 // ---------------------------------------------------------------------------
-template <bool DK>
 __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int QBLK = kQb * D * 2;  // 8 KB
-  __shared__ __attribute__((aligned(1024))) char ktile[kTile * D * 2];  // 32 KB
   __shared__ __attribute__((aligned(1024))) char q0b[QBLK];
   __shared__ __attribute__((aligned(1024))) char q1b[QBLK];
   __shared__ __attribute__((aligned(1024))) char g0b[QBLK];
   __shared__ __attribute__((aligned(1024))) char g1b[QBLK];
   __shared__ __attribute__((aligned(256))) float st0[2 * 64];  // lse2, delta of a block (+ slack)
   __shared__ __attribute__((aligned(256))) float st1[2 * 64];
+  __shared__ __attribute__((aligned(1024))) char vtile[kTile * D * 2];  // the tile's V rows, 32 KB
 
   const Tile tile = map_tile(p, true);
   if (!tile.valid) return;
@@ -407,31 +377,32 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
                                                (r0 + lane) * 4, 0, 0, 0);
     }
   };
+  // K rows of this wave's 32 keys (B operand of S) stay in VGPRs for the
+  // whole sweep (rows past N read as 0); the tile's V rows go to LDS.
+  const int kj = k0 + 32 * w + l32;
+  bf16x8 kreg[NKK];
   {
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * D), 0, N * D * 2, kBufDword3);
-    stage_rows<32>(krs, ktile, k0, N, w, lane);
+    const bool ok = kj < N;
+    const u32x4* ks = reinterpret_cast<const u32x4*>(p.k + (head + (ok ? kj : 0)) * D + 8 * hf);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) kreg[kk] = __builtin_bit_cast(bf16x8, ok ? ks[2 * kk] : u32x4{0, 0, 0, 0});
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + head * D), 0, N * D * 2, kBufDword3);
+    stage_rows<32>(vrs, vtile, k0, N, w, lane);
   }
   if (nblk > 0) load_block(0, q0b, g0b, st0);
-
-  // V rows of this wave's keys as B operands of dP (rows past N read as 0).
-  const int kj = k0 + 32 * w + l32;
-  bf16x8 vreg[NKK];
-  if constexpr (DK) {
-    const bool ok = kj < N;
-    const u32x4* vs = reinterpret_cast<const u32x4*>(p.v + (head + (ok ? kj : 0)) * D + 8 * hf);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) vreg[kk] = __builtin_bit_cast(bf16x8, ok ? vs[2 * kk] : u32x4{0, 0, 0, 0});
-  }
   const float c = p.c;
   const int ja = k0 + 32 * w, jb = ja + 31;
   const int qrow = perm_key(l32);
   const TrOff tro = tr_offsets(lane);
 
-  f32x16 acc[NMD];  // dK^T or dV^T
+  f32x16 acck[NMD], accv[NMD];  // dK^T, dV^T
 #pragma unroll
   for (int md = 0; md < NMD; ++md)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[md][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) {
+      acck[md][r] = 0.0f;
+      accv[md][r] = 0.0f;
+    }
 
   auto block = [&](int j, const char* ql, const char* gl, const float* sl) {
     const int i0 = (qb_lo + j) * kQb;
@@ -444,71 +415,50 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
     }
     // Fragments are read one k-step ahead of their MFMAs (sched_barrier keeps
     // the compiler from hoisting every read, which would not fit in VGPRs).
-    bf16x8 kf = row_frag(ktile, 32 * w + l32, 0, hf), qf = row_frag(ql, qrow, 0, hf), gf = kf;
-    if constexpr (DK) gf = row_frag(gl, qrow, 0, hf);
+    // (Fragments are read just before their MFMA: read-ahead registers are
+    // what the two accumulators need.)
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      bf16x8 kn = kf, qn = qf, gn = gf;
-      if (kk + 1 < NKK) {
-        kn = row_frag(ktile, 32 * w + l32, kk + 1, hf);
-        qn = row_frag(ql, qrow, kk + 1, hf);
-        if constexpr (DK) gn = row_frag(gl, qrow, kk + 1, hf);
-      }
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf, s, 0, 0, 0);
-      if constexpr (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gf, vreg[kk], dp, 0, 0, 0);
-      kf = kn;
-      qf = qn;
-      gf = gn;
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ql, qrow, kk, hf), kreg[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(gl, qrow, kk, hf), row_frag(vtile, 32 * w + l32, kk, hf), dp,
+                                                   0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Register r holds query i0 + 16 (r / 8) + 8 hf + r % 8 of key kj.
-    const bool full = (i0 + kQb <= N) && all_visible(p, jmax, i0, i0 + kQb - 1, ja, jb);
-    const Band bd = band(p, i0 + 8 * hf - kj);   // i - j = base + off
-    const bool kvis = kj < jmax;
-    const int ilim = N - i0 - 8 * hf;            // query offset limit
-    // B operands: P (for dV) or dS = P (dP - D) (for dK), bf16.
-    bf16x8 pb[2];
+    mask_klane(p, jmax, N, kj, ja, jb, hf, s, i0);
+    // B operands: P (for dV) and dS = P (dP - D) (for dK), bf16.
+    bf16x8 pb[2], pv[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(sl + 16 * t + 8 * hf);
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(sl + 16 * t + 8 * hf + 4);
-      f32x4 d0, d1;
-      if constexpr (DK) {
-        d0 = *reinterpret_cast<const f32x4*>(sl + 64 + 16 * t + 8 * hf);
-        d1 = *reinterpret_cast<const f32x4*>(sl + 64 + 16 * t + 8 * hf + 4);
-      }
-      f32x8 f;
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(sl + 64 + 16 * t + 8 * hf);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(sl + 64 + 16 * t + 8 * hf + 4);
+      f32x8 f, fp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * t + e;
-        const int off = 16 * t + e;
         const float l2 = e < 4 ? l0[e] : l1[e - 4];
-        float x = s[r];
-        if (!full) {
-          const bool vis = kvis & (off < ilim) & (off > bd.lo) & (off <= bd.hi);
-          x = vis ? x : kNegInf;
-        }
-        const float pr = fast_exp2(fmaf(x, c, -l2));
-        if constexpr (DK) {
-          const float dl = e < 4 ? d0[e] : d1[e - 4];
-          f[e] = pr * (dp[r] - dl);
-        } else {
-          f[e] = pr;
-        }
+        const float pr = fast_exp2(fmaf(s[r], c, -l2));
+        const float dl = e < 4 ? d0[e] : d1[e - 4];
+        fp[e] = pr;
+        f[e] = pr * (dp[r] - dl);
       }
       pb[t] = __builtin_convertvector(f, bf16x8);
+      pv[t] = __builtin_convertvector(fp, bf16x8);
     }
-    // dV^T += dO^T P or dK^T += Q^T dS, 16 queries per MFMA; the transposed
-    // fragments are read one step ahead.
-    const char* tl = DK ? ql : gl;
-    bf16x8 fa = tr_frag(tl, tro, 0, 0);
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA (dO and Q read
+    // transposed).
 #pragma unroll
     for (int i = 0; i < 2 * NMD; ++i) {
-      const int md = i >> 1, t = i & 1;
-      bf16x8 fn = fa;
-      if (i + 1 < 2 * NMD) fn = tr_frag(tl, tro, (i + 1) >> 1, (i + 1) & 1);
-      acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, pb[t], acc[md], 0, 0, 0);
-      fa = fn;
+      accv[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(gl, tro, i >> 1, i & 1), pv[i & 1], accv[i >> 1], 0,
+                                                             0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NMD; ++i) {
+      acck[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ql, tro, i >> 1, i & 1), pb[i & 1], acck[i >> 1], 0,
+                                                             0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -526,22 +476,23 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
     iter(j + 1, q1b, g1b, st1, q0b, g0b, st0);
   }
   if (j < nblk) iter(j, q0b, g0b, st0, q1b, g1b, st1);
-  // With no query block the K tile's loads were never waited for; no load
-  // into LDS may still be in flight when the workgroup ends.
+  // No load into LDS may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  if (kj < N) {
-    __bf16* dst = (DK ? p.dk : p.dv) + (head + kj) * D;
-    const float f = DK ? p.scale : 1.0f;
+  auto store = [&](__bf16* dst, const f32x16 (&a)[NMD], float f) {
 #pragma unroll
     for (int md = 0; md < NMD; ++md)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         u32x2 wv;
-        wv[0] = pack_bf16x2(acc[md][4 * rq + 0] * f, acc[md][4 * rq + 1] * f);
-        wv[1] = pack_bf16x2(acc[md][4 * rq + 2] * f, acc[md][4 * rq + 3] * f);
+        wv[0] = pack_bf16x2(a[md][4 * rq + 0] * f, a[md][4 * rq + 1] * f);
+        wv[1] = pack_bf16x2(a[md][4 * rq + 2] * f, a[md][4 * rq + 3] * f);
         *reinterpret_cast<u32x2*>(dst + 32 * md + 8 * rq + 4 * hf) = wv;
       }
+  };
+  if (kj < N) {
+    store(p.dk + (head + kj) * D, acck, p.scale);
+    store(p.dv + (head + kj) * D, accv, 1.0f);
   }
 }
 
@@ -577,10 +528,7 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, (long long)rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(grid), dim3(kT), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(grid), dim3(kT), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid), dim3(kT), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kT), 0, stream, p);

@@ -7,6 +7,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "masks.h"
 #include "tile_layout.h"
 
 namespace osfa {
@@ -129,62 +130,11 @@ __device__ __forceinline__ bool rows_see_all(const FwdParams& p, int jmax, int q
 
 
 // Masks of one 64-key block of scores held as S^T accumulators (register r
-// of group kt holds key j0 + 32 kt + 16 (r / 8) + 8 hf + r % 8 of query
-// qi): nothing when every query of the wave's rows [qa, qb] sees every key;
-// per 32-key half, all -inf when no row sees it, otherwise one or two
-// compares per score against the query's bounds on the key offset.
+// of group kt holds key j0 + 32 kt + 16 (r / 8) + 8 hf + r % 8 of query qi).
 __device__ __forceinline__ void mask_block(const FwdParams& p, const KeyRange& kr, int qi, int qa, int qb, int hf,
                                            f32x16 (&s)[2], int j0) {
   if (rows_see_all(p, kr.jmax, qa, qb, j0)) return;
-  int hi = kr.jmax - 1 - j0;                                 // padding: j < jmax
-  int hi_min = hi, hi_max = hi;                              // over the wave's rows
-  if (p.causal) {
-    hi = min(hi, qi - j0);                                   // j <= i
-    hi_min = min(hi_min, qa - j0);
-    hi_max = min(hi_max, qb - j0);
-  }
-  int lo = -1 - kBc, lo_min = -1 - kBc, lo_max = -1 - kBc;
-  if (p.window > 0) {
-    lo = qi - p.window - j0;                                 // i - j < window
-    lo_min = qa - p.window - j0;
-    lo_max = qb - p.window - j0;
-    if (!p.causal) {
-      hi = min(hi, qi + p.window - 1 - j0);                  // j - i < window
-      hi_min = min(hi_min, qa + p.window - 1 - j0);
-      hi_max = min(hi_max, qb + p.window - 1 - j0);
-    }
-  }
-  lo -= 8 * hf;
-  hi -= 8 * hf;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int t0 = 32 * kt, t1 = 32 * kt + 31;
-    if (hi_max < t0 || lo_min >= t1) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = kNegInf;
-      continue;
-    }
-    const bool need_hi = hi_min < t1, need_lo = lo_max >= t0;
-    if (need_hi && need_lo) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 16 * (r >> 3) + (r & 7);
-        s[kt][r] = ((t > lo) & (t <= hi)) ? s[kt][r] : kNegInf;
-      }
-    } else if (need_hi) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 16 * (r >> 3) + (r & 7);
-        s[kt][r] = (t <= hi) ? s[kt][r] : kNegInf;
-      }
-    } else if (need_lo) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 16 * (r >> 3) + (r & 7);
-        s[kt][r] = (t > lo) ? s[kt][r] : kNegInf;
-      }
-    }
-  }
+  mask_qlane_cut(p, kr.jmax, qi, qa, qb, hf, s, j0);
 }
 
 FwdParams make_params(const FwdArgs& a, int br) {
