@@ -5,7 +5,7 @@
 // prove it is exact", "What interviewers probe next"; page "Online softmax
 // for a whole query tile, matrix form", "What interviewers probe next").
 //
-//   D_i  = sum_d dO_id O_id                      (bwd_prep_kernel)
+//   D_i  = sum_d dO_id O_id                      (bwd_dq_kernel, for both)
 //   dP   = dO V^T,  dS = P * (dP - D_i)          (the softmax Jacobian)
 //   dQ   = scale dS K                             (bwd_dq_kernel: query tiles)
 //   dV   = P^T dO                                  (bwd_dkdv_kernel: key tiles)
@@ -154,33 +154,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* blk, const TrOff& t, int m
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id and LSE_i in log2 units (+inf for a row with no key,
-// so that exp2(s - lse2) is 0 there).  16 lanes per row, 16 rows per block.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long rows) {
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int part = threadIdx.x & 15;
-  float acc = 0.0f;
-  if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + 8 * part);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + row * D + 8 * part);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf16_lo(a[e]), bf16_lo(g[e]), acc);
-      acc = fmaf(bf16_hi(a[e]), bf16_hi(g[e]), acc);
-    }
-  }
-  // Sum over the 16 lanes of the row.
-#pragma unroll
-  for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
-  if (row < rows && part == 0) {
-    p.delta[row] = acc;
-    const float l = p.lse[row];
-    p.lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dQ: query tiles of 128, key blocks of 64.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
@@ -231,8 +204,30 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
       doreg[kk] = __builtin_bit_cast(bf16x8, qok ? gs[2 * kk] : u32x4{0, 0, 0, 0});
     }
   }
-  const float lse2 = qok ? p.lse2[head + qi] : __builtin_huge_valf();
-  const float dlt = qok ? p.delta[head + qi] : 0.0f;
+  // D_i = sum_d dO_id O_id (this half's 64 columns, then the other half's)
+  // and LSE in log2 units (+inf for a row with no key, so exp2(s - lse2) is
+  // 0 there); written to the workspace for bwd_dkdv_kernel, which runs next.
+  float dlt = 0.0f;
+  {
+    const u32x4* os = reinterpret_cast<const u32x4*>(p.o + (head + (qok ? qi : 0)) * D + 8 * hf);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4 a = qok ? os[2 * kk] : u32x4{0, 0, 0, 0};
+      const u32x4 g = __builtin_bit_cast(u32x4, doreg[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dlt = fmaf(bf16_lo(a[e]), bf16_lo(g[e]), dlt);
+        dlt = fmaf(bf16_hi(a[e]), bf16_hi(g[e]), dlt);
+      }
+    }
+  }
+  dlt = sum_halves(dlt);
+  const float lse_in = qok ? p.lse[head + qi] : kNegInf;
+  const float lse2 = lse_in == kNegInf ? __builtin_huge_valf() : lse_in * kLog2e;
+  if (qok && hf == 0) {
+    p.delta[head + qi] = dlt;
+    p.lse2[head + qi] = lse2;
+  }
   const float c = p.c;
   const int qa = q0 + 32 * w, qb = qa + 31;
   const int krow = perm_key(l32);
@@ -525,13 +520,11 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   p.n_tiles = (a.N + kTile - 1) / kTile;
   p.total = a.B * a.H * p.n_tiles;
   const unsigned grid = (unsigned)((p.total + 7) / 8 * 8);
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, (long long)rows);
-  hipError_t e = hipGetLastError();
+  // dQ first: it also writes D and LSE log2(e), which bwd_dkdv_kernel reads.
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kT), 0, stream, p);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid), dim3(kT), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kT), 0, stream, p);
   return hipGetLastError();
 }
 
