@@ -27,18 +27,19 @@ COPY_BYTES = 1 << 30  # the calibration copy moves 1 GiB each way
 
 # Kernel-name pattern -> the sources that define it (for the staleness hash).
 KERNEL_SOURCES = {
-    "fwd_bf16_d128_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/device_common.h", "csrc/tile_layout.h"],
-    "fwd_bf16_kernel": ["csrc/attn_fwd.hip", "csrc/device_common.h"],
-    "fwd_f32_kernel": ["csrc/attn_fwd.hip", "csrc/device_common.h"],
+    "fwd_bf16_d128_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h",
+                             "csrc/tile_layout.h"],
+    "fwd_bf16_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h"],
+    "fwd_f32_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h"],
+    "fwd_fp8_d128_kernel": ["csrc/attn_fwd_fp8.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h",
+                            "csrc/tile_layout.h"],
     "decode_partial_kernel": ["csrc/decode.hip", "csrc/device_common.h"],
     "decode_merge_kernel": ["csrc/decode.hip", "csrc/device_common.h"],
     "softmax_rows_reg_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
     "softmax_rows_stream_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
     "softmax_topk_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
-    "fwd_fp8_d128_kernel": ["csrc/attn_fwd_fp8.hip", "csrc/fwd_common.h", "csrc/device_common.h"],
-    "bwd_prep_kernel": ["csrc/attn_bwd.hip", "csrc/device_common.h", "csrc/tile_layout.h"],
-    "bwd_dq_kernel": ["csrc/attn_bwd.hip", "csrc/device_common.h", "csrc/tile_layout.h"],
-    "bwd_dkdv_kernel": ["csrc/attn_bwd.hip", "csrc/device_common.h", "csrc/tile_layout.h"],
+    "bwd_dq_kernel": ["csrc/attn_bwd.hip", "csrc/masks.h", "csrc/device_common.h", "csrc/tile_layout.h"],
+    "bwd_dkdv_kernel": ["csrc/attn_bwd.hip", "csrc/masks.h", "csrc/device_common.h", "csrc/tile_layout.h"],
 }
 
 
@@ -48,7 +49,7 @@ def short_name(name: str) -> str:
         return f"decode_partial_kernel<{'bf16' if m.group(1) == 'DF16b' else 'f32'}, {m.group(2)}>"
     m = re.search(r"(fwd_bf16_d128_kernel<[^>]*>|fwd_bf16_kernel<\d+>|fwd_f32_kernel<\d+>|"
                   r"decode_partial_kernel\w*|decode_merge_kernel<\d+>|softmax_topk_kernel<\d, (?:true|false)>|"
-                  r"softmax_rows_\w+<[\d, ]+>|bwd_dkdv_kernel|bwd_dq_kernel|bwd_prep_kernel|fwd_fp8_d128_kernel|"
+                  r"softmax_rows_\w+<[\d, ]+>|bwd_dkdv_kernel|bwd_dq_kernel|fwd_fp8_d128_kernel|"
                   r"__amd_rocclr_copyBuffer|copyBuffer)", name)
     if m:
         return m.group(1)
