@@ -202,7 +202,7 @@ __device__ __forceinline__ float unord_f(int b) { return __builtin_bit_cast(floa
 template <int W, bool WITH_Y>
 __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x, float* y, float* topv,
                                                                    int32_t* topi, int cols, int k) {
-  constexpr int U = 8;
+  constexpr int U = 4;
   constexpr int STEP = kSmThreads * U;
   const int row = blockIdx.x;
   const float* xr = x + (size_t)row * cols;
@@ -241,6 +241,43 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
     }
   };
 
+  // Per-wave candidate queue, room for every slot of a chunk (it cannot
+  // overflow); a wave only touches its own row of it, so the LDS writes of
+  // the lanes and the reads of the drain need no barrier, only the wave's
+  // own ordering of LDS operations.
+  constexpr int kQueue = 64 * U * W;
+  __shared__ float lm_s[kSmThreads];  // lane maxima of the first chunk
+  __shared__ float qv_s[kSmWaves][kQueue];
+  __shared__ int qi_s[kSmWaves][kQueue];
+  auto drain = [&](int n) {
+    for (int q = 0; q < n; ++q) {
+      const float cx = qv_s[w][q];
+      const int ci = qi_s[w][q];
+      if (!better(cx, ci, Tx, Ti) && !(cx == Tx && Ti == 0x7fffffff)) continue;  // wave-uniform
+      // Insert: lanes whose entry is worse than the candidate take the
+      // previous lane's entry, or the candidate if the previous is better.
+      const bool mine = better(cx, ci, lx, li);
+      const float px = dpp_f<0x111>(kNegInf, lx);  // lane i - 1 (row 0 holds the list)
+      const int pi = dpp_i<0x111>(0x7fffffff, li);
+      const bool prev_better = lane > 0 && better(px, pi, cx, ci);
+      if (mine && lane < 16) {
+        if (lane == 0 || prev_better) {
+          lx = cx;
+          li = ci;
+        } else {
+          lx = px;
+          li = pi;
+        }
+      }
+      const float kx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), k - 1));
+      const int ki = __builtin_amdgcn_readlane(li, k - 1);
+      if (better(kx, ki, Tx, Ti) || (kx == Tx && Ti == 0x7fffffff && ki != 0x7fffffff)) {
+        Tx = kx;
+        Ti = ki;
+      }
+    }
+  };
+
   auto process = [&](int base, float (&v)[U][W]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -256,16 +293,28 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
     fold_chunk(r, mx, &v[0][0], U * W);
 
     if (base == 0) {
-      // Threshold from the first chunk: the k-th largest lane maximum
-      // (groups of equal maxima are counted together).
-      float lm = mx;
+      // Threshold from the first chunk: the k-th largest of the 256 lane
+      // maxima of the workgroup (k elements reach it, so nothing below it is
+      // in the row's top k; groups of equal maxima are counted together).
+      // One barrier; every wave starts from the same bound.
+      lm_s[threadIdx.x] = mx;
+      __syncthreads();
+      float a4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a4[t] = lm_s[lane + 64 * t];
       int cnt = 0;
       while (true) {
-        const float M = wave_max_bcast(lm);
+        const float M = wave_max_bcast(fmaxf(fmaxf(a4[0], a4[1]), fmaxf(a4[2], a4[3])));
         if (M == kNegInf) break;  // fewer than k elements in this chunk
-        const uint64_t eq = __ballot(lm == M);
-        cnt += __builtin_popcountll(eq);
-        lm = (lm == M) ? kNegInf : lm;
+        int c = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          c += a4[t] == M ? 1 : 0;
+          a4[t] = a4[t] == M ? kNegInf : a4[t];
+        }
+        // sum of c over the wave (c in [0, 4]) by four ballots
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cnt += __builtin_popcountll(__ballot(c > t));
         if (cnt >= k) {
           Tx = M;
           break;
@@ -278,46 +327,32 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
     const float Tf = fmaxf(Tx, unord_f(__builtin_amdgcn_readfirstlane(t_shared)));
     // Nothing in the chunk reaches the threshold: no slot needs a look.
     if (__ballot((mx >= Tf) & (mx != kNegInf)) == 0) return;
-    // One ballot per register slot: only lanes whose value in that slot
-    // reaches the threshold are visited, so the cost follows the number of
-    // candidates, not the chunk size.  Slots past the row hold -inf and never
-    // qualify.
+    // Candidates (values reaching the threshold) go to this wave's queue in
+    // LDS: one compare per register slot, a ballot, and a write by the lanes
+    // that have one; the insertion is then one copy of code run once per
+    // candidate.  (Inlining the insertion in every slot made this kernel
+    // larger than the instruction cache.)  Slots past the row hold -inf and
+    // never qualify.
+    const float T = fmaxf(Tx, Tf);
+    int n = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int a0 = base + w * 64 + kSmThreads * u;  // access index of lane 0
 #pragma unroll
       for (int e = 0; e < W; ++e) {
-        uint64_t mask = __ballot((v[u][e] >= fmaxf(Tx, Tf)) & (v[u][e] != kNegInf));
-        while (mask) {
-          const int src = __builtin_ctzll(mask);
-          mask &= mask - 1;
-          const float cx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[u][e]), src));
-          const int ci = (a0 + src) * W + e;
-          if (!better(cx, ci, Tx, Ti) && !(cx == Tx && Ti == 0x7fffffff)) continue;  // wave-uniform
-          // Insert: lanes whose entry is worse than the candidate take the
-          // previous lane's entry, or the candidate if the previous is better.
-          const bool mine = better(cx, ci, lx, li);
-          const float px = dpp_f<0x111>(kNegInf, lx);  // lane i - 1 (row 0 holds the list)
-          const int pi = dpp_i<0x111>(0x7fffffff, li);
-          const bool prev_better = lane > 0 && better(px, pi, cx, ci);
-          if (mine && lane < 16) {
-            if (lane == 0 || prev_better) {
-              lx = cx;
-              li = ci;
-            } else {
-              lx = px;
-              li = pi;
-            }
-          }
-          const float kx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), k - 1));
-          const int ki = __builtin_amdgcn_readlane(li, k - 1);
-          if (better(kx, ki, Tx, Ti) || (kx == Tx && Ti == 0x7fffffff && ki != 0x7fffffff)) {
-            Tx = kx;
-            Ti = ki;
-          }
+        const bool c = (v[u][e] >= T) & (v[u][e] != kNegInf);
+        const uint64_t mask = __ballot(c);
+        if (mask == 0) continue;  // wave-uniform
+        if (c) {
+          const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          qv_s[w][pos] = v[u][e];
+          qi_s[w][pos] = (a0 + lane) * W + e;
         }
+        n += __builtin_popcountll(mask);
       }
     }
+    drain(n);
   };
 
   // Chunks are taken in pairs; a pair's second chunk may lie wholly past the
@@ -341,12 +376,19 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
     ci_s[w * k + lane] = li;
   }
   __syncthreads();
-  if (w == 0 && lane < kSmWaves * k) {
-    const float mx = cx_s[lane];
-    const int mi = ci_s[lane];
+  if (w == 0) {
+    // Lane l holds candidate l; its rank counts the better candidates, each
+    // broadcast from its lane (no LDS round trip per comparison).
+    const int nk = kSmWaves * k;
+    const float mx = lane < nk ? cx_s[lane] : kNegInf;
+    const int mi = lane < nk ? ci_s[lane] : 0x7fffffff;
     int rank = 0;
-    for (int j = 0; j < kSmWaves * k; ++j) rank += better(cx_s[j], ci_s[j], mx, mi) ? 1 : 0;
-    if (rank < k) {
+    for (int j = 0; j < nk; ++j) {
+      const float bx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), j));
+      const int bi = __builtin_amdgcn_readlane(mi, j);
+      rank += better(bx, bi, mx, mi) ? 1 : 0;
+    }
+    if (lane < nk && rank < k) {
       topv[(size_t)row * k + rank] = fast_exp2(fmaf(mx, kLog2e, -r.m)) / r.d;
       topi[(size_t)row * k + rank] = mi;
     }
