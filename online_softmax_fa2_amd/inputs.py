@@ -232,6 +232,27 @@ def decode_slice(seed: int, b: int, h: int, Nkv: int, d: int, dtype: str = "bf16
     return q, k, v, None, None, None
 
 
+def attn_bits_large(B: int, H: int, N: int, d: int, regions, *, seed: int = 0, count: int = 3) -> list[np.ndarray]:
+    """``count`` bfloat16 tensors [B, H, N, d] (Q, K, V, then dO) as bit patterns, for the largest shapes.
+
+    Zero except the row ranges ``regions`` = [(b, h, r0, r1), ...], whose
+    elements are a random sign, a binade drawn uniformly from [1/8, 1/4),
+    [1/4, 1/2), [1/2, 1), [1, 2) and a uniform 7-bit mantissa (integer
+    operations on one uniform 16-bit draw), so that tensors of 10^9 elements
+    cost only their allocation; range i is drawn from rng([seed, 3000, t, i]).
+    """
+    out = []
+    for t in range(count):
+        bits = np.zeros((B, H, N, d), np.uint16)
+        for i, (b, h, r0, r1) in enumerate(regions):
+            rng = np.random.default_rng([seed, 3000, t, i])
+            r = rng.integers(0, 1 << 16, size=(r1 - r0, d), dtype=np.uint16)
+            e = ((r >> 7) & np.uint16(3)) + np.uint16(124)  # biased exponents 124..127
+            bits[b, h, r0:r1] = (r & np.uint16(0x807F)) | (e << np.uint16(7))
+        out.append(bits)
+    return out
+
+
 def softmax_rows_inputs(rows: int, cols: int, *, seed: int = 0, sigma: float = 4.0) -> np.ndarray:
     """x[rows, cols] float32, i.i.d. N(0, sigma^2), drawn in blocks of 256 rows."""
     x = np.empty((rows, cols), np.float32)

@@ -79,6 +79,15 @@ def per_kernel_counter(path: str) -> dict[str, dict[str, float]]:
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
 
 
+def per_kernel_duration_ns(path: str) -> dict[str, float]:
+    """Mean dispatch duration (ns) per kernel from the counter CSV's timestamps."""
+    acc: dict[str, dict[str, float]] = defaultdict(dict)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc[short_name(r["Kernel_Name"])][r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return {k: sum(v.values()) / len(v) for k, v in acc.items() if v}
+
+
 def copy_factor(path: str, counter: str) -> float:
     vals = []
     with open(path) as f:
@@ -135,11 +144,16 @@ def sq(counters_csv: str, out_txt: str, command: str, n_xcd: int = 8, n_simd: in
     pipe was busy; GRBM_GUI_ACTIVE sums the active GPU cycles over the XCDs.
     SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_LDS and SQ_ACTIVE_INST_VALU are
     wave-cycle totals (same unit), so their ratios are fractions of wave time.
+    clock_GHz is the active cycles of one XCD over the dispatch duration: the
+    shader clock the kernel actually ran at (mfma_busy% is relative to it).
     """
     k = per_kernel_counter(counters_csv)
-    lines = ["# rocprofv3 SQ counters per kernel (averages per dispatch)", f"# command: {command}", "",
+    dur = per_kernel_duration_ns(counters_csv)
+    lines = ["# rocprofv3 SQ counters per kernel (averages per dispatch)", f"# command: {command}",
+             "# clock_GHz = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; dispatches shorter than ~50 us overstate it",
+             "# (the counters' window is longer than the dispatch)", "",
              f"{'kernel':44s} {'mfma_TFLOP':>10s} {'mfma_busy%':>10s} {'wait_any%':>9s} {'wait_lds%':>9s} "
-             f"{'valu%':>6s} {'lds_bank_conf':>14s}"]
+             f"{'valu%':>6s} {'lds_bank_conf':>14s} {'clock_GHz':>9s}"]
     for name, c in sorted(k.items()):
         if family(name) is None:
             continue
@@ -149,7 +163,7 @@ def sq(counters_csv: str, out_txt: str, command: str, n_xcd: int = 8, n_simd: in
         wc = c.get("SQ_WAVE_CYCLES", 0.0) or 1.0
         lines.append(f"{name[:44]:44s} {flop / 1e12:10.4f} {100 * busy:10.1f} {100 * c.get('SQ_WAIT_ANY', 0) / wc:9.1f} "
                      f"{100 * c.get('SQ_WAIT_INST_LDS', 0) / wc:9.1f} {100 * c.get('SQ_ACTIVE_INST_VALU', 0) / wc:6.1f} "
-                     f"{c.get('SQ_LDS_BANK_CONFLICT', 0):14.0f}")
+                     f"{c.get('SQ_LDS_BANK_CONFLICT', 0):14.0f} {active / dur.get(name, float('inf')):9.2f}")
     open(out_txt, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import online_softmax_fa2_amd as osfa
-from online_softmax_fa2_amd.inputs import WORKLOADS, attn_inputs, workload_attn_inputs
+from online_softmax_fa2_amd.inputs import WORKLOADS, attn_bits_large, attn_inputs, bf16_bits_to_f32, workload_attn_inputs
 from oracle import attention_ref
 from tests.gpu_util import (Guarded, assert_bf16_out, assert_f32_rel, assert_lse_abs, assert_normwise, upload_bf16,
                             upload_f32)
@@ -151,3 +151,39 @@ def test_fwd_full_bf16_window_pad_8192():
     inp, O, L = _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0), (0, 63)], nrows=48)
     # every query sees at least itself or the keys before the padding: no -inf rows here
     assert np.all(np.isfinite(L))
+
+
+def test_fwd_bf16_largest_offsets():
+    """Three heads of 2^22 + 37 queries (d = 128): the last head starts past byte 2^31 of each tensor.
+
+    Q, K, V are random on the rows of the sampled blocks and their visible
+    keys (start, middle and end of the first and the last head) and zero
+    elsewhere, so a read from a wrong offset changes a sampled result.  The
+    oracle solves the sub-problem of each block's visible keys (causal and
+    window masks only depend on i - j, so a shifted slice reproduces them).
+    """
+    B, H, N, d, W, M = 1, 3, (1 << 22) + 37, 128, 100, 48
+    kvl = N - 50
+    blocks = [(h, s) for h in (0, 2) for s in (0, N // 2 + 5, N - M)]
+    regions = [(0, h, max(0, s - W + 1), s + M) for h, s in blocks]
+    qb, kb, vb = attn_bits_large(B, H, N, d, regions, seed=77)
+    q, k, v = upload_bf16(qb), upload_bf16(kb), upload_bf16(vb)
+    assert 2 * N * d * 2 > 2**31  # byte offset of the last head
+    scale = 1.0 / np.sqrt(d)
+    o = Guarded((B, H, N, d), torch.bfloat16)
+    lse = Guarded((B, H, N), torch.float32)
+    osfa.attn_fwd(q, k, v, scale=scale, causal=True, window=W, kv_len=torch.tensor([kvl], dtype=torch.int32,
+                  device="cuda:0"), out=o.t, lse=lse.t)
+    torch.cuda.synchronize()
+    o.check()
+    lse.check()
+    for (h, s), (_, _, lo, hi) in zip(blocks, regions):
+        sl = (slice(0, 1), slice(h, h + 1), slice(lo, hi))
+        Or, Lr = attention_ref(bf16_bits_to_f32(qb[sl]), bf16_bits_to_f32(kb[sl]), bf16_bits_to_f32(vb[sl]),
+                               scale, causal=True, window=W, kv_len=[max(0, min(kvl, hi) - lo)],
+                               rows=np.arange(s - lo, s - lo + M))
+        og = o.t[0, h, s:s + M].float().cpu().numpy()
+        lg = lse.t[0, h, s:s + M].cpu().numpy()
+        what = f"h={h} rows {s}..{s + M - 1}"
+        assert_bf16_out(og, Or[0, 0], what=what + " O")
+        assert_lse_abs(lg, Lr[0, 0], 1e-3, what=what + " LSE")

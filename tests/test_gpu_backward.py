@@ -21,7 +21,8 @@ import pytest
 import torch
 
 import online_softmax_fa2_amd as osfa
-from online_softmax_fa2_amd.inputs import WORKLOADS, attn_inputs, grad_inputs, workload_attn_inputs
+from online_softmax_fa2_amd.inputs import (WORKLOADS, attn_bits_large, attn_inputs, bf16_bits_to_f32, grad_inputs,
+                                          workload_attn_inputs)
 from oracle import attention_bwd_error_bound, attention_bwd_ref, visible_mask
 from tests.gpu_util import Guarded, upload_bf16
 
@@ -136,3 +137,43 @@ def test_bwd_full_bf16_causal_2048():
 
 def test_bwd_full_bf16_window_pad_8192():
     _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0), (0, 63)])
+
+
+def test_bwd_largest_offsets():
+    """Three heads of 2^22 + 37 queries (d = 128, causal, window 100, padding): the last head starts past
+    byte 2^31 of every tensor.
+
+    Q, K, V, dO are random on the sampled blocks' dependency ranges (the W - 1
+    rows before a block and after it) and zero elsewhere: a zero query with a
+    zero dO adds nothing to dK, dV, so the oracle's sub-problem on that range
+    gives the exact gradients of the block's rows, and a read from a wrong
+    offset changes them.
+    """
+    B, H, N, d, W, M = 1, 3, (1 << 22) + 37, 128, 100, 48
+    kvl = N - 50
+    blocks = [(h, s) for h in (0, 2) for s in (0, N // 2 + 5, N - M - 60)]  # the last keys are padding
+    regions = [(0, h, max(0, s - W + 1), min(N, s + M + W - 1)) for h, s in blocks]
+    qb, kb, vb, dob = attn_bits_large(B, H, N, d, regions, seed=78, count=4)
+    q, k, v, dout = upload_bf16(qb), upload_bf16(kb), upload_bf16(vb), upload_bf16(dob)
+    assert 2 * N * d * 2 > 2**31
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    kv = torch.tensor([kvl], dtype=torch.int32, device="cuda:0")
+    o, lse = osfa.attn_fwd(q, k, v, scale=scale, causal=True, window=W, kv_len=kv)
+    grads = [Guarded((B, H, N, d), torch.bfloat16) for _ in range(3)]
+    ws = Guarded((osfa.bwd_workspace_bytes(B, H, N) // 4,), torch.float32)
+    osfa.attn_bwd(q, k, v, o, dout, lse, scale=scale, causal=True, window=W, kv_len=kv, dq=grads[0].t,
+                  dk=grads[1].t, dv=grads[2].t, workspace=ws.t)
+    torch.cuda.synchronize()
+    for g in grads:
+        g.check()
+    ws.check()
+    for (h, s), (_, _, lo, hi) in zip(blocks, regions):
+        sl = (slice(0, 1), slice(h, h + 1), slice(lo, hi))
+        args = tuple(bf16_bits_to_f32(a[sl]) for a in (qb, kb, vb, dob)) + (scale,)
+        kw = dict(causal=True, window=W, kv_len=[max(0, min(kvl, hi) - lo)])
+        ref = attention_bwd_ref(*args, **kw)
+        bnd = attention_bwd_error_bound(*args, **kw)
+        r = slice(s - lo, s - lo + M)
+        for name, g, rf, bd in zip(("dQ", "dK", "dV"), grads, ref, bnd):
+            got = g.t[0, h, s:s + M].float().cpu().numpy()
+            assert_grad(got, rf[0, 0, r], bd[0, 0, r], f"h={h} rows {s}..{s + M - 1} {name}")

@@ -2,7 +2,7 @@
 import numpy as np
 import torch
 
-from online_softmax_fa2_amd.inputs import (attn_inputs, bf16_bits_to_f32, bf16_round,
+from online_softmax_fa2_amd.inputs import (attn_bits_large, attn_inputs, bf16_bits_to_f32, bf16_round,
                                            decode_inputs, decode_slice, softmax_rows_inputs)
 
 
@@ -44,3 +44,19 @@ def test_softmax_inputs_blocks_are_independent_of_row_count():
     a = softmax_rows_inputs(300, 40, seed=1)
     b = softmax_rows_inputs(600, 40, seed=1)
     assert np.array_equal(a, b[:300])
+
+
+def test_attn_bits_large_regions():
+    regions = [(0, 1, 5, 40), (1, 0, 0, 3)]
+    a = attn_bits_large(2, 2, 64, 16, regions, seed=3, count=4)
+    b = attn_bits_large(2, 2, 64, 16, regions, seed=3, count=4)
+    assert len(a) == 4 and all(np.array_equal(x, y) for x, y in zip(a, b))
+    for x in a:
+        v = bf16_bits_to_f32(x)
+        mask = np.zeros(v.shape, bool)
+        for bb, h, r0, r1 in regions:
+            mask[bb, h, r0:r1] = True
+        assert np.all(v[~mask] == 0)
+        m = np.abs(v[mask])
+        assert m.min() >= 0.125 and m.max() < 2.0 and (v[mask] < 0).any() and (v[mask] > 0).any()
+    assert not np.array_equal(a[0], a[1])
