@@ -24,6 +24,9 @@ namespace {
 
 constexpr int kSmThreads = 256;
 constexpr int kSmWaves = kSmThreads / 64;
+// Rows of at most 4096 aligned floats, at least 16 per CU: one wave per row
+// (else a workgroup per row).
+constexpr bool kSoftmaxWavePerRow = true;
 
 // Element access, 4-wide when the row allows it.  ld/st go through the
 // caches; ld_nt/st_nt mark data touched exactly once (non-temporal) so it does
@@ -118,6 +121,49 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_reg_kernel(const floa
 #pragma unroll
       for (int e = 0; e < W; ++e) o[e] = fast_exp2(fmaf(v[i][e], kLog2e, -r.m)) * inv;
       st_nt<W>(yr + (size_t)a * W, o);
+    }
+  }
+}
+
+// Rows of up to 64 x VPT 4-float accesses, one wave per row (4 rows per
+// workgroup): lane l owns accesses l + 64 i, the pair is merged across the
+// wave only (no LDS, no barrier), and a launch over a few thousand rows has
+// every row's loads in flight at once instead of a workgroup per row in two
+// rounds.
+template <int VPT>
+__global__ __launch_bounds__(kSmThreads) void softmax_rows_wave_kernel(const float* x, float* y, int rows, int cols) {
+  const int row = blockIdx.x * kSmWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const float* xr = x + (size_t)row * cols;
+  float* yr = y + (size_t)row * cols;
+  const int nacc = cols / 4;
+  float v[VPT][4];
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int a = lane + 64 * i;
+    if (a < nacc) {
+      ld_nt<4>(xr + (size_t)a * 4, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[i][e] = kNegInf;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[i][e]);
+  }
+  MD r{kNegInf, 0.0f};
+  fold_chunk(r, mx, &v[0][0], VPT * 4);  // -inf slots contribute exp2(-inf) = 0
+  r = wave_md_merge(r);
+  const float inv = 1.0f / r.d;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int a = lane + 64 * i;
+    if (a < nacc) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = fast_exp2(fmaf(v[i][e], kLog2e, -r.m)) * inv;
+      st_nt<4>(yr + (size_t)a * 4, o);
     }
   }
 }
@@ -403,7 +449,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 hipError_t launch_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream) {
   const bool vec = (cols % 4 == 0) && aligned16(x) && aligned16(y);
   const dim3 grid(rows), block(kSmThreads);
-  if (vec) {
+  if (vec && kSoftmaxWavePerRow && cols / 4 <= 64 * 16 && rows >= 16 * 256) {
+    const int nacc = cols / 4;
+    const dim3 wgrid((rows + kSmWaves - 1) / kSmWaves);
+    if (nacc <= 64 * 4)
+      hipLaunchKernelGGL((softmax_rows_wave_kernel<4>), wgrid, block, 0, stream, x, y, rows, cols);
+    else if (nacc <= 64 * 8)
+      hipLaunchKernelGGL((softmax_rows_wave_kernel<8>), wgrid, block, 0, stream, x, y, rows, cols);
+    else
+      hipLaunchKernelGGL((softmax_rows_wave_kernel<16>), wgrid, block, 0, stream, x, y, rows, cols);
+  } else if (vec) {
     const int nacc = cols / 4;
     if (nacc <= 256)
       hipLaunchKernelGGL((softmax_rows_reg_kernel<4, 1>), grid, block, 0, stream, x, y, cols);
