@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "decode_partial_kernel": ["csrc/decode.hip", "csrc/device_common.h"],
     "decode_merge_kernel": ["csrc/decode.hip", "csrc/device_common.h"],
     "softmax_rows_reg_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
+    "softmax_rows_wave_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
     "softmax_rows_stream_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
     "softmax_topk_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
     "bwd_dq_kernel": ["csrc/attn_bwd.hip", "csrc/masks.h", "csrc/device_common.h", "csrc/tile_layout.h"],
