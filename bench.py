@@ -10,7 +10,9 @@ One step runs every kernel of the path once, each on its own workload:
     workload for a seeded dO, from the O and LSE the forward wrote, counted
     at 10 d FLOPs per visible query-key pair;
   * attn_fwd_fp8 (not part of `value`): the headline workload with Q, K, V
-    quantized per tensor to e4m3, against the FP8 matrix-core peak.
+    quantized per tensor to e4m3, against the FP8 matrix-core peak;
+  * attn_fwd_exp2_offload (not part of `value`): the headline workload with
+    one exponential pair in four computed on the FMA pipes.
 Inputs are seeded synthetic data already resident in HBM.  Each kernel is
 bracketed by HIP events on the stream it is launched on; `value` is the
 forward pass's algorithmic TFLOP/s (4 d FLOPs per visible query-key pair)
@@ -98,6 +100,8 @@ def main():
     del f8.q, f8.k, f8.v
     f8o = torch.empty_like(fo)
     f8lse = torch.empty_like(flse)
+    po = torch.empty_like(fo)
+    plse = torch.empty_like(flse)
 
     # --- decode workload --------------------------------------------------------
     dw_name = "decode_bf16_b1h32_nkv131072_d128_split64"
@@ -151,6 +155,9 @@ def main():
                                                         f8o.data_ptr(), f8lse.data_ptr(), fw["B"], fw["H"], fw["N"],
                                                         fw["d"], f8.scale, f8.qd, f8.kd, f8.vd, 1, fw["window"],
                                                         fkv.data_ptr(), sh))),
+        ("attn_fwd_exp2_offload", lambda: check(lib.attn_fwd_exp2_offload(
+            fq.data_ptr(), fk.data_ptr(), fv.data_ptr(), po.data_ptr(), plse.data_ptr(), fw["B"], fw["H"], fw["N"],
+            fw["d"], fin.scale, 1, fw["window"], fkv.data_ptr(), 4, sh))),
         ("attn_bwd", lambda: check(lib.attn_bwd(1, fq.data_ptr(), fk.data_ptr(), fv.data_ptr(), fo.data_ptr(),
                                                 bdo.data_ptr(), flse.data_ptr(), bdq.data_ptr(), bdk.data_ptr(),
                                                 bdv.data_ptr(), fw["B"], fw["H"], fw["N"], fw["d"], fin.scale, 1,
@@ -192,6 +199,7 @@ def main():
     tk_gbs = tk_bytes / (ms["online_softmax_topk_rows"] * 1e-3) / 1e9
     bwd_tflops = bw_flops / (ms["attn_bwd"] * 1e-3) / 1e12
     f8_tflops = fw_flops / (ms["attn_fwd_fp8"] * 1e-3) / 1e12
+    px_tflops = fw_flops / (ms["attn_fwd_exp2_offload"] * 1e-3) / 1e12
 
     cpu = cpu_baseline(fin, fw, args.cpu_seconds)
 
@@ -200,7 +208,7 @@ def main():
     # of the kernel sources: reported only while the kernel is unchanged.
     from online_softmax_fa2_amd.rocprof_summary import lookup
     traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
-    fwd_traffic = lookup("fwd_bf16_d128_kernel", traffic_file)
+    fwd_traffic = lookup("fwd_bf16_d128_kernel<4, 0>", traffic_file)
     dec_traffic = lookup("decode_partial_kernel", traffic_file)
 
     out = {
@@ -222,7 +230,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": acc.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / acc.PEAK_BF16_TFLOPS, 4),
                      "traffic": None if fwd_traffic is None else round(fwd_traffic),
-                     "kernel": "fwd_bf16_d128_kernel<4>", "avg_launch_us": round(ms["attn_fwd"] * 1e3, 2)},
+                     "kernel": "fwd_bf16_d128_kernel<4, 0>", "avg_launch_us": round(ms["attn_fwd"] * 1e3, 2)},
         "kernels": {
             "attn_fwd": {"workload": fw_name, "avg_us": round(ms["attn_fwd"] * 1e3, 2),
                          "min_us": round(ms_min["attn_fwd"] * 1e3, 2), "tflops": round(fwd_tflops, 2),
@@ -245,6 +253,11 @@ def main():
             "attn_fwd_fp8": {"workload": fw_name + " (e4m3 Q, K, V)", "avg_us": round(ms["attn_fwd_fp8"] * 1e3, 2),
                              "min_us": round(ms_min["attn_fwd_fp8"] * 1e3, 2), "tflops": round(f8_tflops, 2),
                              "frac_mfma_peak": round(f8_tflops / acc.PEAK_FP8_TFLOPS, 4)},
+            "attn_fwd_exp2_offload": {"workload": fw_name + " (1 exp pair in 4 on the FMA pipes)",
+                                      "avg_us": round(ms["attn_fwd_exp2_offload"] * 1e3, 2),
+                                      "min_us": round(ms_min["attn_fwd_exp2_offload"] * 1e3, 2),
+                                      "tflops": round(px_tflops, 2),
+                                      "frac_mfma_peak": round(px_tflops / acc.PEAK_BF16_TFLOPS, 4)},
             "attn_bwd": {"workload": fw_name, "avg_us": round(ms["attn_bwd"] * 1e3, 2),
                          "min_us": round(ms_min["attn_bwd"] * 1e3, 2), "tflops": round(bwd_tflops, 2),
                          "frac_mfma_peak": round(bwd_tflops / acc.PEAK_BF16_TFLOPS, 4),

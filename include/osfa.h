@@ -82,6 +82,28 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
                        int causal, int window, const int32_t* kv_len, hipStream_t stream);
 
 /*
+ * attn_fwd_exp2_offload -- attn_fwd for bf16, d = 128, with part of the
+ * exponentials computed on the FMA pipes: FlashAttention-4's answer to
+ * exponential units that lag the matrix cores (page "Derive online softmax,
+ * prove it is exact", "What interviewers probe next").  Of every poly_every
+ * consecutive pairs of exponentials a lane forms for a key block, the last
+ * pair is 2^n * p(f) (x = n + f, |f| <= 1/2, p a cubic with relative error
+ * <= 7.5e-5, 2^n by v_ldexp_f32) instead of v_exp_f32; the rest is attn_fwd
+ * exactly.  Results agree with attn_fwd to within that error, far below the
+ * bf16 rounding of P and O.  On gfx950 the polynomial costs eight VALU
+ * instructions against one transcendental, so this variant is slower than
+ * attn_fwd there; it exists to measure the trade.
+ *
+ * Arguments, layout, masks and errors: as attn_fwd with dtype = bf16.
+ * poly_every: 2, 4 or 8 (one exponential in 2, 4 or 8 on the FMA pipes;
+ * others -> ATTN_ERR_UNSUPPORTED).  Supported: d = 128 (others ->
+ * ATTN_ERR_UNSUPPORTED); Q, K, V, O 16-byte aligned.
+ */
+attn_status_t attn_fwd_exp2_offload(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                    int N, int d, float scale, int causal, int window, const int32_t* kv_len,
+                                    int poly_every, hipStream_t stream);
+
+/*
  * attn_fwd_fp8 -- attn_fwd with FP8 inputs: Q, K, V are OCP e4m3 (e4m3fn)
  * codes, one byte per element, and each tensor has one float32 descale, so
  * that the value of an element is code x descale.  Computes the same O and

@@ -39,6 +39,8 @@ def load_library() -> ctypes.CDLL:
     p, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [i, p, p, p, p, p, i, i, i, i, f, i, i, p, p]
     lib.attn_fwd.restype = i
+    lib.attn_fwd_exp2_offload.argtypes = [p, p, p, p, p, i, i, i, i, f, i, i, p, i, p]
+    lib.attn_fwd_exp2_offload.restype = i
     lib.attn_fwd_fp8.argtypes = [p, p, p, p, p, i, i, i, i, f, f, f, f, i, i, p, p]
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
@@ -104,6 +106,29 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, window: 
         raise ValueError("kv_len must be int32 [B]")
     _check(load_library().attn_fwd(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                                    float(scale), int(bool(causal)), int(window), _ptr(kv_len), _stream(stream)))
+    return out, lse
+
+
+def attn_fwd_exp2_offload(q, k, v, poly_every: int, scale: float | None = None, causal: bool = False,
+                          window: int = 0, kv_len=None, out=None, lse=None, stream=None):
+    """attn_fwd for bf16 [B, H, N, 128] with one exponential in poly_every (2, 4, 8) on the FMA pipes."""
+    _need_device(q, k, v, kv_len, out, lse)
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B):
+        raise ValueError("kv_len must be int32 [B]")
+    _check(load_library().attn_fwd_exp2_offload(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                                float(scale), int(bool(causal)), int(window), _ptr(kv_len),
+                                                int(poly_every), _stream(stream)))
     return out, lse
 
 

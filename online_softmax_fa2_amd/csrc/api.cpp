@@ -58,6 +58,29 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
   return hip_status(e, "attn_fwd");
 }
 
+attn_status_t attn_fwd_exp2_offload(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                    int N, int d, float scale, int causal, int window, const int32_t* kv_len,
+                                    int poly_every, hipStream_t stream) {
+  if (poly_every != 2 && poly_every != 4 && poly_every != 8)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_exp2_offload: poly_every=%d not built (2, 4 or 8)", poly_every);
+  if (!Q || !K || !V || !O || !LSE) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: null tensor pointer");
+  if (B < 1 || H < 1 || N < 1 || d < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: sizes must be >= 1 (B=%d H=%d N=%d d=%d)", B, H, N, d);
+  if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_exp2_offload: head dim d=%d not built (128)", d);
+  if ((long long)B * H * N * d >= kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: B*H*N*d too large");
+  if ((long long)B * H >= (1LL << 24)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: B*H too large");
+  if ((long long)N * d >= (1LL << 30))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: N*d must be < 2^30 (one head)");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: scale must be finite and > 0 (got %g)", (double)scale);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: causal must be 0 or 1");
+  if (window < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: window must be >= 0 (0 = no window)");
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: Q, K, V, O must be 16-byte aligned");
+  osfa::FwdArgs a{Q, K, V, O, LSE, kv_len, B, H, N, d, scale, causal, window};
+  return hip_status(osfa::launch_attn_fwd_bf16_exp2_offload(a, poly_every, stream), "attn_fwd_exp2_offload");
+}
+
 attn_status_t attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
                            int d, float scale, float q_descale, float k_descale, float v_descale, int causal,
                            int window, const int32_t* kv_len, hipStream_t stream) {

@@ -308,7 +308,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 // LDS fragment reads are issued this many MFMA slots ahead of their use.
 constexpr int KAHEAD = 4, VAHEAD = 4;
 
-template <int NW>
+// POLY > 0: in every group of POLY consecutive pairs of exponentials of a
+// half block, the last pair is computed by exp2_fma (the FMA-pipe
+// exponential); POLY = 0: all on v_exp_f32.
+template <int NW, int POLY>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) {
   constexpr int D = 128;
   constexpr int BLK = kBc * D * 2;  // one K or V block: 16 KB
@@ -460,6 +463,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
   };
   // exp2 of half a block (the 16 registers of one kt) against the current
   // reference, packed to bf16; the row sum is taken in float32.
+  // Pair q (registers 2q, 2q + 1) of a half block takes the FMA-pipe
+  // exponential in the POLY variants.
+  auto on_fma = [](int q) { return POLY > 0 && q % POLY == POLY - 1; };
   auto exp_half = [&](f32x16& s, bf16x8 (&pk)[2]) {
     const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
     float part[2] = {0.0f, 0.0f};
@@ -467,7 +473,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     for (int t = 0; t < 2; ++t) {
       f32x8 f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = fast_exp2(fmaf(s[8 * t + e], c, -mr));
+      for (int e = 0; e < 8; ++e) {
+        const float x = fmaf(s[8 * t + e], c, -mr);
+        f[e] = on_fma(4 * t + e / 2) ? exp2_fma(x) : fast_exp2(x);
+      }
       pk[t] = __builtin_convertvector(f, bf16x8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) part[t] += f[e];
@@ -515,8 +524,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
     OSFA_KEEP(s[2 * p + 1]);
   };
   auto st2 = [&](f32x16& s, int p) {
-    s[2 * p] = fast_exp2(s[2 * p]);
-    s[2 * p + 1] = fast_exp2(s[2 * p + 1]);
+    if (on_fma(p)) {
+      s[2 * p] = exp2_fma(s[2 * p]);
+      s[2 * p + 1] = exp2_fma(s[2 * p + 1]);
+    } else {
+      s[2 * p] = fast_exp2(s[2 * p]);
+      s[2 * p + 1] = fast_exp2(s[2 * p + 1]);
+    }
     OSFA_KEEP(s[2 * p]);
     OSFA_KEEP(s[2 * p + 1]);
   };
@@ -891,11 +905,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdParams p) {
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 128) {
     const FwdParams p = make_params(a, 32 * kV2Waves);
-    hipLaunchKernelGGL((fwd_bf16_d128_kernel<kV2Waves>), dim3(grid_for(p)), dim3(64 * kV2Waves), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_d128_kernel<kV2Waves, 0>), dim3(grid_for(p)), dim3(64 * kV2Waves), 0, stream, p);
   } else {
     const FwdParams p = make_params(a, kBr);
     hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid_for(p)), dim3(kThreads), 0, stream, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_bf16_exp2_offload(const FwdArgs& a, int poly_every, hipStream_t stream) {
+  const FwdParams p = make_params(a, 32 * kV2Waves);
+  const dim3 grid(grid_for(p)), block(64 * kV2Waves);
+  if (poly_every == 2)
+    hipLaunchKernelGGL((fwd_bf16_d128_kernel<kV2Waves, 2>), grid, block, 0, stream, p);
+  else if (poly_every == 4)
+    hipLaunchKernelGGL((fwd_bf16_d128_kernel<kV2Waves, 4>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_d128_kernel<kV2Waves, 8>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

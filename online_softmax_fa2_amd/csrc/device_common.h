@@ -28,6 +28,27 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// 2^x on the FMA pipes instead of the transcendental unit (the exponential
+// offload of FlashAttention-4, page "Derive online softmax, prove it is
+// exact", "What interviewers probe next"): split x = n + f with n the
+// nearest integer and |f| <= 1/2, take 2^f from a cubic whose coefficients
+// minimize the maximum relative error on [-1/2, 1/2] (a linear program on a
+// dense grid, exp2_poly.py; 7.5e-5 with float32 coefficients, below the
+// 2^-9 rounding of a bf16 P), and apply 2^n with v_ldexp_f32.  Arguments
+// below -200 (masked scores: -inf) give exactly 0.  Eight VALU instructions
+// (max, rndne, sub, 3 fma, cvt, ldexp) against one v_exp_f32.
+constexpr float kExp2C0 = 0.9999280571937561f;
+constexpr float kExp2C1 = 0.6932608485221863f;
+constexpr float kExp2C2 = 0.24261115491390228f;
+constexpr float kExp2C3 = 0.05517221987247467f;
+__device__ __forceinline__ float exp2_fma(float x) {
+  x = fmaxf(x, -200.0f);
+  const float n = __builtin_rintf(x);
+  const float f = x - n;
+  const float p = fmaf(fmaf(fmaf(kExp2C3, f, kExp2C2), f, kExp2C1), f, kExp2C0);
+  return __builtin_amdgcn_ldexpf(p, (int)n);
+}
+
 // Exchange across the two 32-lane halves with v_permlane32_swap.  With
 // operands (a, b) both holding x, the instruction leaves lane l < 32 with
 // (x[l], x[l + 32]) and lane l >= 32 with (x[l - 32], x[l]).  The compiler

@@ -23,6 +23,8 @@ struct FwdArgs {
 // Each returns the hipError_t of its launch(es).
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// bf16, d = 128: one exponential pair in every poly_every (2, 4 or 8) on the FMA pipes.
+hipError_t launch_attn_fwd_bf16_exp2_offload(const FwdArgs& a, int poly_every, hipStream_t stream);
 // e4m3 Q, K, V (d = 128), bf16 O: scores take scale * qk_descale, O takes v_descale.
 hipError_t launch_attn_fwd_fp8(const FwdArgs& a, float qk_descale, float v_descale, hipStream_t stream);
 

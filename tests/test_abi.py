@@ -83,6 +83,32 @@ def test_attn_fwd_rejects(lib, kw, status, msg):
     assert msg in lib.attn_last_error().decode()
 
 
+def _exp2_offload(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=FAKE, B=1, H=1, N=16, d=128, scale=0.1, causal=0, window=0,
+             kv_len=None, poly_every=4, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_exp2_offload(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["d"],
+                                     a["scale"], a["causal"], a["window"], a["kv_len"], a["poly_every"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(poly_every=3), bd.ATTN_ERR_UNSUPPORTED, "poly_every"),
+    (dict(poly_every=0), bd.ATTN_ERR_UNSUPPORTED, "poly_every"),
+    (dict(poly_every=16), bd.ATTN_ERR_UNSUPPORTED, "poly_every"),
+    (dict(d=64), bd.ATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(V=None), bd.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(N=0), bd.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(scale=float("nan")), bd.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(causal=5), bd.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(window=-1), bd.ATTN_ERR_INVALID_ARG, "window"),
+    (dict(O=FAKE + 8), bd.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(N=1 << 23), bd.ATTN_ERR_INVALID_ARG, "one head"),
+])
+def test_exp2_offload_rejects(lib, kw, status, msg):
+    assert _exp2_offload(lib, **kw) == status
+    assert msg in lib.attn_last_error().decode()
+
+
 def test_workspace_bytes(lib):
     assert lib.attn_decode_splitkv_workspace_bytes(1, 32, 128, 64) == 32 * 64 * 130 * 4
     assert lib.attn_decode_splitkv_workspace_bytes(2, 3, 64, 7) == 2 * 3 * 7 * 66 * 4

@@ -18,7 +18,8 @@ from tests.gpu_util import (Guarded, assert_bf16_out, assert_f32_rel, assert_lse
 pytestmark = pytest.mark.gpu
 
 
-def run_fwd(inp):
+def run_fwd(inp, poly_every=0):
+    """attn_fwd, or attn_fwd_exp2_offload when poly_every > 0 (bf16 only)."""
     if inp.dtype == "bf16":
         q, k, v = upload_bf16(inp.q_bits), upload_bf16(inp.k_bits), upload_bf16(inp.v_bits)
         odt = torch.bfloat16
@@ -29,7 +30,12 @@ def run_fwd(inp):
     o = Guarded((B, H, N, d), odt)
     lse = Guarded((B, H, N), torch.float32)
     kvl = None if inp.kv_len is None else torch.from_numpy(inp.kv_len).to("cuda:0")
-    osfa.attn_fwd(q, k, v, scale=inp.scale, causal=inp.causal, window=inp.window, kv_len=kvl, out=o.t, lse=lse.t)
+    if poly_every:
+        osfa.attn_fwd_exp2_offload(q, k, v, poly_every, scale=inp.scale, causal=inp.causal, window=inp.window,
+                                   kv_len=kvl, out=o.t, lse=lse.t)
+    else:
+        osfa.attn_fwd(q, k, v, scale=inp.scale, causal=inp.causal, window=inp.window, kv_len=kvl, out=o.t,
+                      lse=lse.t)
     torch.cuda.synchronize()
     o.check()
     lse.check()
@@ -122,11 +128,11 @@ def test_fwd_closed_forms_bf16():
     assert np.all(O == 1.0)
 
 
-def _full(name, heads, nrows=64):
+def _full(name, heads, nrows=64, poly_every=0):
     w = WORKLOADS[name]
-    print(f"attn_fwd full workload {name}", flush=True)
+    print(f"attn_fwd full workload {name} poly_every={poly_every}", flush=True)
     inp = workload_attn_inputs(name)
-    O, L = run_fwd(inp)
+    O, L = run_fwd(inp, poly_every)
     assert not np.isnan(O).any() and not np.isnan(L).any()
     check(inp, O, L, heads=heads)
     rng = np.random.default_rng(123)
@@ -135,6 +141,23 @@ def _full(name, heads, nrows=64):
     all_heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
     check(inp, O, L, rows=rows, heads=all_heads[::5])
     return inp, O, L
+
+
+@pytest.mark.parametrize("poly_every", [2, 4, 8])
+@pytest.mark.parametrize("case", [c for c in CASES if c[3] == 128], ids=[f"c{i}" for i, c in enumerate(CASES) if c[3] == 128])
+def test_fwd_exp2_offload_parity(case, poly_every):
+    """The variant with part of the exponentials on the FMA pipes meets the same bar as attn_fwd."""
+    B, H, N, d, causal, window, kv_len, n_big = case
+    print(f"attn_fwd_exp2_offload poly_every={poly_every} B={B} H={H} N={N} causal={causal} window={window}", flush=True)
+    inp = attn_inputs(B, H, N, d, dtype="bf16", seed=200 + N, causal=causal, window=window, kv_len=kv_len,
+                      n_big_keys=n_big)
+    O, L = run_fwd(inp, poly_every)
+    check(inp, O, L)
+
+
+def test_fwd_exp2_offload_full_window_pad_8192():
+    """The variant in the launch configuration the benchmark times (one pair in four on the FMA pipes)."""
+    _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0)], nrows=48, poly_every=4)
 
 
 def test_fwd_full_f32_n1000():
