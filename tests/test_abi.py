@@ -250,3 +250,16 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         bd.online_softmax_rows(x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every entry point raises instead of computing anything."""
+    import torch
+    import online_softmax_fa2_amd as osfa
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "libosfa.so"))
+    monkeypatch.setattr(bd, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        bd.load_library()
+    x = torch.zeros(4, 8)
+    with pytest.raises((RuntimeError, ValueError)):
+        osfa.online_softmax_rows(x)
