@@ -63,11 +63,6 @@ __device__ __forceinline__ HalfPair permlane32_pair(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
   return HalfPair{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
 }
-// Value held by lane (l xor 32).
-__device__ __forceinline__ float swap_halves(float x) {
-  const HalfPair p = permlane32_pair(x);
-  return (__lane_id() < 32) ? p.hi : p.lo;
-}
 // max / sum of x over lanes l and l xor 32 (order-independent, no lane test).
 // Maxima of scores and running maxima (finite or -inf, never NaN).  The
 // device code is built with -fno-honor-nans, so the compiler turns fmaxf
@@ -120,13 +115,6 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s, 64);
-  return x;
-}
-
-// All-reduction over each aligned group of 16 lanes.
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int s = 1; s < 16; s <<= 1) x += __shfl_xor(x, s, 64);
   return x;
 }
 
