@@ -209,6 +209,11 @@ def main():
     from online_softmax_fa2_amd.rocprof_summary import lookup
     traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
     fwd_traffic = lookup("fwd_bf16_d128_kernel<4, 0>", traffic_file)
+    # Shader clock the forward kernel ran at (GRBM_GUI_ACTIVE per XCD over the
+    # dispatch time, profiles/sq_counters.json): the matrix-core peak at that
+    # clock is the nominal one scaled by clock / 2.4 GHz.
+    sq_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sq_counters.json")
+    fwd_clock = lookup("fwd_bf16_d128_kernel<4, 0>", sq_file, "clock_ghz")
     dec_traffic = lookup("decode_partial_kernel", traffic_file)
 
     out = {
@@ -230,7 +235,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": acc.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / acc.PEAK_BF16_TFLOPS, 4),
                      "traffic": None if fwd_traffic is None else round(fwd_traffic),
-                     "kernel": "fwd_bf16_d128_kernel<4, 0>", "avg_launch_us": round(ms["attn_fwd"] * 1e3, 2)},
+                     "kernel": "fwd_bf16_d128_kernel<4, 0>", "avg_launch_us": round(ms["attn_fwd"] * 1e3, 2),
+                     "clock_ghz_measured": None if fwd_clock is None else round(fwd_clock, 3),
+                     "frac_at_measured_clock": None if fwd_clock is None else
+                     round(fwd_tflops / (acc.PEAK_BF16_TFLOPS * fwd_clock / acc.NOMINAL_CLOCK_GHZ), 4)},
         "kernels": {
             "attn_fwd": {"workload": fw_name, "avg_us": round(ms["attn_fwd"] * 1e3, 2),
                          "min_us": round(ms_min["attn_fwd"] * 1e3, 2), "tflops": round(fwd_tflops, 2),

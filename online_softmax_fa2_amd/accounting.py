@@ -12,6 +12,7 @@ import numpy as np
 
 # MI355X published peaks.
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+NOMINAL_CLOCK_GHZ = 2.4     # the shader clock the published peaks assume
 PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3    # fp32 vector
 PEAK_HBM_GBS = 8000.0       # HBM3E

@@ -137,7 +137,8 @@ def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_txt, out_j
     print("\n".join(lines))
 
 
-def sq(counters_csv: str, out_txt: str, command: str, n_xcd: int = 8, n_simd: int = 1024) -> None:
+def sq(counters_csv: str, out_txt: str, command: str, out_json: str | None = None, n_xcd: int = 8,
+       n_simd: int = 1024) -> None:
     """MFMA and stall evidence per kernel from SQ counters.
 
     SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512-FLOP units of bf16 MFMA work;
@@ -155,6 +156,7 @@ def sq(counters_csv: str, out_txt: str, command: str, n_xcd: int = 8, n_simd: in
              "# (the counters' window is longer than the dispatch)", "",
              f"{'kernel':44s} {'mfma_TFLOP':>10s} {'mfma_busy%':>10s} {'wait_any%':>9s} {'wait_lds%':>9s} "
              f"{'valu%':>6s} {'lds_bank_conf':>14s} {'clock_GHz':>9s}"]
+    table = {}
     for name, c in sorted(k.items()):
         if family(name) is None:
             continue
@@ -165,12 +167,17 @@ def sq(counters_csv: str, out_txt: str, command: str, n_xcd: int = 8, n_simd: in
         lines.append(f"{name[:44]:44s} {flop / 1e12:10.4f} {100 * busy:10.1f} {100 * c.get('SQ_WAIT_ANY', 0) / wc:9.1f} "
                      f"{100 * c.get('SQ_WAIT_INST_LDS', 0) / wc:9.1f} {100 * c.get('SQ_ACTIVE_INST_VALU', 0) / wc:6.1f} "
                      f"{c.get('SQ_LDS_BANK_CONFLICT', 0):14.0f} {active / dur.get(name, float('inf')):9.2f}")
+        table[name] = {"clock_ghz": active / dur.get(name, float("inf")), "mfma_busy": busy,
+                       "dispatch_ns": dur.get(name), "source_sha256": source_sha(family(name))}
     open(out_txt, "w").write("\n".join(lines) + "\n")
+    if out_json:
+        json.dump(table, open(out_json, "w"), indent=1, sort_keys=True)
     print("\n".join(lines))
 
 
-def lookup(kernel_prefix: str, path: str) -> float | None:
-    """HBM bytes per launch for the kernel, or None if absent or measured on different sources."""
+def lookup(kernel_prefix: str, path: str, field: str = "bytes") -> float | None:
+    """A recorded per-launch figure of the kernel (HBM bytes by default), or None if absent or measured on
+    different sources."""
     try:
         table = json.load(open(path))
     except (OSError, ValueError):
@@ -178,8 +185,8 @@ def lookup(kernel_prefix: str, path: str) -> float | None:
     for k, v in table.items():
         if k.startswith(kernel_prefix):
             fam = family(k)
-            if fam and v.get("source_sha256") == source_sha(fam):
-                return float(v["bytes"])
+            if fam and v.get("source_sha256") == source_sha(fam) and v.get(field) is not None:
+                return float(v[field])
     return None
 
 
@@ -189,6 +196,6 @@ if __name__ == "__main__":
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:9])
     elif sys.argv[1] == "sq":
-        sq(*sys.argv[2:5])
+        sq(*sys.argv[2:6])
     else:
         raise SystemExit(__doc__)
