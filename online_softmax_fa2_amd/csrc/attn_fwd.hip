@@ -307,6 +307,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
 // LDS fragment reads are issued this many MFMA slots ahead of their use.
 constexpr int KAHEAD = 4, VAHEAD = 4;
+// float32 launches with fewer 128-query tiles than this use the key-split kernel.
+constexpr long long kSplitTilesBelow = 256;
 
 // POLY > 0: in every group of POLY consecutive pairs of exponentials of a
 // half block, the last pair is computed by exp2_fma (the FMA-pipe
@@ -900,6 +902,166 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdParams p) {
 }
 
 
+
+// ---------------------------------------------------------------------------
+// float32, few query tiles: the waves of a workgroup split the key range
+//
+// When a launch has fewer 128-query tiles than the chip has CUs, the tile
+// kernel above leaves most SIMDs idle.  Here a workgroup owns 32 queries and
+// its S waves take the 32-key blocks of their range in turn (wave w: blocks
+// w, w + S, ...), each staging its blocks in its own LDS region (no
+// barrier), and each keeps its own partial (m, l, O).  At the end the S
+// partial states are merged through LDS by the rescale rule of split-KV
+// (page "Derive online softmax, prove it is exact", "What interviewers probe
+// next"; article "Online softmax", Step 4): M = max m_w, O = sum 2^(m_w - M)
+// O_w / sum 2^(m_w - M) l_w.
+// ---------------------------------------------------------------------------
+
+template <int D, int S>
+__global__ __launch_bounds__(64 * S, 1) void fwd_f32_split_kernel(FwdParams p) {
+  constexpr int BC = 32;        // keys per block
+  constexpr int RS = D + 4;     // LDS row stride (floats), +16 B pad
+  constexpr int NKK = D / 2;
+  constexpr int NMD = D / 32;
+  constexpr int WREG = 2 * BC * RS;  // floats of one wave's region (K and V rows)
+  static_assert(32 * (D + 2) <= WREG, "the merge state fits in a wave's region");
+  __shared__ __attribute__((aligned(16))) float lds[S * WREG];
+
+  const Tile tile = map_tile(p);
+  if (!tile.valid) return;
+  const int b = tile.bh / p.H;
+  const int q0 = tile.q0;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int N = p.N;
+  const size_t head_off = (size_t)tile.bh * (size_t)N * D;
+  const float* Kg = static_cast<const float*>(p.k) + head_off;
+  const float* Vg = static_cast<const float*>(p.v) + head_off;
+
+  // MFMA step kk pairs d = kk (lower half) with d = kk + D/2 (upper half).
+  const int qi = q0 + l32;
+  float qreg[NKK];
+  {
+    const bool ok = qi < N;
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) + head_off +
+                                                      (size_t)(ok ? qi : 0) * D + (D / 2) * hf);
+#pragma unroll
+    for (int i = 0; i < NKK / 4; ++i) {
+      f32x4 v = ok ? src[i] : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qreg[4 * i + e] = v[e];
+    }
+  }
+
+  const KeyRange kr = key_range(p, b, q0);
+  const int kb_lo = kr.kbeg / BC;
+  const int kb_hi = (kr.kend > kr.kbeg) ? (kr.kend + BC - 1) / BC : kb_lo;
+  float* ks = lds + w * WREG;
+  float* vs = ks + BC * RS;
+
+  f32x16 oacc[NMD];
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
+  float m_run = kNegInf, l_run = 0.0f;
+  const float c = p.c;
+
+  for (int kb = kb_lo + w; kb < kb_hi; kb += S) {
+    const int j0 = kb * BC;
+    // This wave's block into its own region (rows past N read row N - 1;
+    // they are masked).  A wave's LDS accesses take effect in order, so the
+    // previous block's reads are done before these writes land.
+    for (int idx = lane; idx < BC * D / 4; idx += 64) {
+      const int row = idx / (D / 4), c4 = idx % (D / 4);
+      const int j = min(j0 + row, N - 1);
+      *reinterpret_cast<f32x4*>(ks + row * RS + 4 * c4) = *reinterpret_cast<const f32x4*>(Kg + (size_t)j * D + 4 * c4);
+      *reinterpret_cast<f32x4*>(vs + row * RS + 4 * c4) = *reinterpret_cast<const f32x4*>(Vg + (size_t)j * D + 4 * c4);
+    }
+    // S^T: lane l, register r holds key j0 + 8 (r/4) + 4 hf + r%4 of query qi.
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    const float* krow = ks + l32 * RS + (D / 2) * hf;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[kk], qreg[kk], s, 0, 0, 0);
+    bool interior = j0 + BC <= kr.jmax;
+    if (p.causal) interior = interior && j0 + BC - 1 <= q0;
+    if (p.window > 0) interior = interior && q0 + 31 - j0 < p.window && (p.causal || j0 + BC - 1 - q0 < p.window);
+    if (!interior) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (!visible(p, kr.jmax, qi, j)) s[r] = kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_ref = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    float rs = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(fmaf(s[r], c, -m_ref));
+      s[r] = e;
+      rs += e;
+    }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+    // O^T += V^T P^T, one key per half per MFMA step.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * RS + 32 * md + l32], s[r], oacc[md], 0, 0, 0);
+    }
+  }
+
+  // This wave's state into its region: m[32], l[32], O[32][D] (query-major).
+  const float l_tot = sum_halves(l_run);
+  float* st = ks;
+  if (hf == 0) {
+    st[l32] = m_run;
+    st[32 + l32] = l_tot;
+  }
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[64 + l32 * D + 32 * md + 8 * (r >> 2) + 4 * hf + (r & 3)] = oacc[md][r];
+  __syncthreads();
+  // Merge: thread t takes elements t, t + 64 S, ... of the tile's 32 x D outputs.
+  for (int e = threadIdx.x; e < 32 * D; e += 64 * S) {
+    const int q = e / D, d = e % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < S; ++u) M = fmaxf(M, lds[u * WREG + q]);
+    float lsum = 0.0f, osum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const float mu = lds[u * WREG + q];
+      const float wgt = (mu == kNegInf) ? 0.0f : fast_exp2(mu - M);
+      lsum += wgt * lds[u * WREG + 32 + q];
+      osum += wgt * lds[u * WREG + 64 + q * D + d];
+    }
+    const int qq = q0 + q;
+    if (qq < N) {
+      static_cast<float*>(p.o)[head_off + (size_t)qq * D + d] = lsum > 0.0f ? osum / lsum : 0.0f;
+      if (d == 0) p.lse[(size_t)tile.bh * N + qq] = lsum > 0.0f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
@@ -926,6 +1088,16 @@ hipError_t launch_attn_fwd_bf16_exp2_offload(const FwdArgs& a, int poly_every, h
 }
 
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  // d = 64 with fewer 128-query tiles than CUs: 32-query workgroups whose 8
+  // waves split the keys.  (The d = 128 instance needs more than 256
+  // registers per lane; built that way it gave wrong rows on causal diagonal
+  // blocks, so d = 128 keeps the tile kernel.)
+  const long long tiles128 = (long long)a.B * a.H * ((a.N + kBr - 1) / kBr);
+  if (a.d == 64 && tiles128 < kSplitTilesBelow) {
+    const FwdParams p = make_params(a, 32);
+    hipLaunchKernelGGL((fwd_f32_split_kernel<64, 8>), dim3(grid_for(p)), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
   const FwdParams p = make_params(a, kBr);
   const dim3 grid(grid_for(p)), block(kThreads);
   if (a.d == 128)

@@ -160,6 +160,20 @@ def test_fwd_exp2_offload_full_window_pad_8192():
     _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0)], nrows=48, poly_every=4)
 
 
+@pytest.mark.parametrize("B,H,N,d,causal,window,kv_len", [
+    (2, 16, 1100, 64, True, 300, [1100, 1000]),
+    (1, 32, 1030, 128, False, 0, None),
+])
+def test_fwd_f32_tile_path(B, H, N, d, causal, window, kv_len):
+    """float32 launches with at least 256 tiles of 128 queries (and every d = 128 one) take the 128-query tile
+    kernel; d = 64 launches with fewer take the key-split kernel, which the other d = 64 cases here run."""
+    assert B * H * ((N + 127) // 128) >= 256
+    print(f"attn_fwd f32 tile path B={B} H={H} N={N} d={d}", flush=True)
+    inp = attn_inputs(B, H, N, d, dtype="f32", seed=N + d, causal=causal, window=window, kv_len=kv_len)
+    O, L = run_fwd(inp)
+    check(inp, O, L, heads=[(0, 0), (B - 1, H - 1), (0, H // 2)])
+
+
 def test_fwd_full_f32_n1000():
     inp = workload_attn_inputs("attn_f32_b1h1_n1000_d64")
     O, L = run_fwd(inp)
