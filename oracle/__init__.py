@@ -34,5 +34,5 @@ invariants and brute force.  No function is "parity unpinned".
 
 from .attention import attention_ref, decode_ref, visible_mask, visible_count  # noqa: F401
 from .softmax import softmax_ref, topk_ref  # noqa: F401
-from .quantized import attention_fp8_error_model  # noqa: F401
+from .quantized import attention_fp8_error_bound, attention_fp8_error_model  # noqa: F401
 from .backward import attention_bwd_ref, attention_bwd_delta, attention_bwd_error_bound  # noqa: F401

@@ -2,8 +2,15 @@
 
 These are not used to check the GPU; they check the pages' own claims
 (exactness, associativity, the invariants) against the direct definitions
-in ``attention`` and ``softmax``.  Each is written from the equations and
-prose of the pages, in their notation, and not from the printed listings.
+in ``attention`` and ``softmax``.  They model the recurrences the pages
+derive, in the pages' notation: ``single_query_blockwise`` the single-query
+recurrence of page "Derive online softmax, prove it is exact", section "A
+strong answer" (written here as a fold of per-block (m, l, a) states under
+the merge rule), and ``blockwise_attention`` the query-tile recurrence of
+page "Online softmax for a whole query tile, matrix form", section "A
+strong answer", whose update equations (running maximum, guarded
+reference, rescale factor, P, l, A) are that page's and so appear here as
+the same few lines.
 
 ``blockwise_attention`` accepts a ``mutation`` name that plants one of the
 mistakes the pages list, so that the tests can show their pins catch it.
@@ -82,27 +89,41 @@ def two_pass_unshifted_softmax(x) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def single_query_blockwise(q, K, V, block: int = 128, scale: float | None = None) -> np.ndarray:
-    """State (m, l, a) after each key block; returns a / l.
+def merge_state(x, y):
+    """Merge two single-query states (m, l, a) by the rescale rule (article "Online softmax", Step 4).
 
-    A block with maximum m~ moves the state to m' = max(m, m~); l and a are
-    both multiplied by exp(m - m') and the block's terms exp(s_i - m') (and
-    exp(s_i - m') v_i) are added.  Starts from (-inf, 0, 0).
+    Both are referenced to the larger maximum; an empty state (-inf, 0, 0)
+    contributes nothing.
+    """
+    (m1, l1, a1), (m2, l2, a2) = x, y
+    M = max(m1, m2)
+    if M == NEG_INF:
+        return NEG_INF, 0.0, a1 + a2
+    w1 = 0.0 if m1 == NEG_INF else math.exp(m1 - M)
+    w2 = 0.0 if m2 == NEG_INF else math.exp(m2 - M)
+    return M, w1 * l1 + w2 * l2, w1 * a1 + w2 * a2
+
+
+def single_query_blockwise(q, K, V, block: int = 128, scale: float | None = None) -> np.ndarray:
+    """The single-query recurrence over key blocks; returns a / l.
+
+    The running state (m, l, a) starts empty; each block contributes its own
+    state (its maximum, the sum of exp(s - max) and the matching weighted
+    sum of V rows), merged into the running one.  Merging is exactly the
+    update of the page: m' = max(m, block max), l and a rescaled by
+    exp(m - m'), the block's terms exp(s_i - m') added.
     """
     q = np.asarray(q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
     sigma = 1.0 / math.sqrt(q.shape[0]) if scale is None else float(scale)
-    m, l = NEG_INF, 0.0
-    a = np.zeros(V.shape[1])
+    state = (NEG_INF, 0.0, np.zeros(V.shape[1]))
     for j0 in range(0, K.shape[0], block):
         s = sigma * (K[j0:j0 + block] @ q)
-        m_new = max(m, float(s.max()))
-        r = math.exp(m - m_new)
-        e = np.exp(s - m_new)
-        l = r * l + float(e.sum())
-        a = r * a + e @ V[j0:j0 + block]
-        m = m_new
+        mb = float(s.max())
+        w = np.exp(s - mb)
+        state = merge_state(state, (mb, float(w.sum()), w @ V[j0:j0 + block]))
+    _, l, a = state
     return a / l
 
 

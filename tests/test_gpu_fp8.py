@@ -3,8 +3,10 @@
 The oracle is the exact attention of the dequantized inputs (code x
 descale), ``oracle.attention_ref``.  The FP8 path differs from it by the
 e4m3 rounding of P and the matrix core's accumulation, which
-``oracle.attention_fp8_error_model`` bounds (pinned on the CPU against a
-simulated FP8 pipeline and planted mistakes).  Per (b, h) slice:
+``oracle.attention_fp8_error_bound`` bounds from the e4m3 and bf16 formats
+alone (pinned on the CPU against simulated FP8 pipelines and planted
+mistakes); no term of it comes from this kernel's design or from a
+measurement.  Per (b, h) slice:
 
   * every element: |O - O_ref| <= 1.5 x the worst-case bound bO;
   * RMS over the slice: rms(O - O_ref) <= 2 rms(sO) + 1.5 rms(bO with the P
@@ -14,6 +16,8 @@ simulated FP8 pipeline and planted mistakes).  Per (b, h) slice:
   * LSE: |LSE - LSE_ref| <= 1.5 x bL (score accumulation error);
   * a query with no visible key: O = 0 and LSE = -inf exactly.
 The factor 1.5 covers the second-order terms the first-order model drops.
+The ratio to ``oracle.attention_fp8_error_model`` (the tighter bound of the
+kernel's own per-block frame) is printed as a diagnostic, not asserted.
 """
 import numpy as np
 import pytest
@@ -21,7 +25,7 @@ import torch
 
 import online_softmax_fa2_amd as osfa
 from online_softmax_fa2_amd.inputs import WORKLOADS, attn_fp8_inputs, bf16_round
-from oracle import attention_fp8_error_model, attention_ref
+from oracle import attention_fp8_error_bound, attention_fp8_error_model, attention_ref
 from tests.gpu_util import Guarded
 
 pytestmark = pytest.mark.gpu
@@ -50,8 +54,9 @@ def check(inp, O, L, heads=None):
         args = (inp.q[sl], inp.k[sl], inp.v[sl], inp.scale)
         kw = dict(causal=inp.causal, window=inp.window, kv_len=None if inp.kv_len is None else inp.kv_len[b:b + 1])
         Or, Lr = attention_ref(*args, **kw)
-        bO, sO, bL = attention_fp8_error_model(*args, **kw)
-        bdet, _, _ = attention_fp8_error_model(*args, **kw, u_p=0.0)
+        bO, sO, bL = attention_fp8_error_bound(*args, **kw)
+        bdet, _, _ = attention_fp8_error_bound(*args, **kw, u_p=0.0)
+        dO = attention_fp8_error_model(*args, **kw)[0][0, 0]
         og, lg = O[b, h], L[b, h]
         Or, Lr, bO, sO, bL, bdet = Or[0, 0], Lr[0, 0], bO[0, 0], sO[0, 0], bL[0, 0], bdet[0, 0]
         what = f"b={b} h={h}"
@@ -60,6 +65,8 @@ def check(inp, O, L, heads=None):
         bad = err > 1.5 * bO
         assert not bad.any(), (f"{what}: {int(bad.sum())} O elements over 1.5 x bound; worst ratio "
                                f"{(err / np.maximum(bO, 1e-300)).max():.3g}")
+        print(f"{what}: worst err / gate {(err / np.maximum(bO, 1e-300)).max():.3f}, "
+              f"worst err / block-frame model {(err / np.maximum(dO, 1e-300)).max():.3f}")
         rms, lim = np.sqrt(np.mean(err ** 2)), 2 * np.sqrt(np.mean(sO ** 2)) + 1.5 * np.sqrt(np.mean(bdet ** 2))
         assert rms <= lim, f"{what}: O rms error {rms:.3e} > {lim:.3e}"
         inf = np.isinf(Lr)

@@ -4,19 +4,22 @@
   finite e4m3fn codes decoded from the format's definition (1 sign, 4
   exponent bits with bias 7, 3 mantissa bits, subnormals, 0x7F/0xFF NaN),
   ties to the even code.
-* ``oracle.attention_fp8_error_model``: a simulated FP8 pipeline (P rounded
-  to e4m3 in a per-(query, 64-key block) power-of-two frame whose block
-  maximum lands in (128, 256], O divided by the sum of the rounded P) stays
-  inside the worst-case bound everywhere and inside the statistical bound in
-  RMS; planted mistakes (a dropped key block, a mask off by one, O not
-  multiplied by the V descale, one frame per row instead of per block on a
-  row dominated by one key) escape one of them.
+* ``oracle.attention_fp8_error_bound`` (the gate, format-derived terms):
+  simulated FP8 pipelines for every legal way of rounding P (no frame, a
+  frame per row, a frame per 64-key block) and with scores carrying a bf16
+  rounding stay inside the worst-case bound everywhere and inside the
+  statistical bound in RMS; planted mistakes (a dropped key block, a mask
+  off by one, O not multiplied by the V descale) escape it; dropping its
+  a_p or kappa term lets a legal pipeline escape.
+* ``oracle.attention_fp8_error_model`` (diagnostic, the block frame's own
+  tighter bound): covers the block-frame pipeline, is never looser than
+  the gate, and rejects a row-wide frame on a row dominated by one key.
 """
 import numpy as np
 import pytest
 
 from online_softmax_fa2_amd.inputs import attn_fp8_inputs, e4m3_descale, e4m3_round
-from oracle import attention_fp8_error_model, attention_ref, visible_mask
+from oracle import attention_fp8_error_bound, attention_fp8_error_model, attention_ref, visible_mask
 
 
 def _e4m3_table():
@@ -72,11 +75,26 @@ def test_e4m3_descale_fits_range():
 
 
 # ---------------------------------------------------------------------------
-# The error model against a simulated FP8 pipeline
+# The gate and the diagnostic model against simulated FP8 pipelines
 # ---------------------------------------------------------------------------
 
-def _sim_fp8(inp, mistake=None):
-    """O of the dequantized inputs with P rounded to e4m3 as the FP8 path does (float64 elsewhere)."""
+def _bf16(x):
+    """Round float64 to the nearest bf16 value (ties to even), via float32."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _sim_fp8(inp, design="block_frame", mistake=None):
+    """O of the dequantized inputs with P rounded to e4m3 (float64 elsewhere).
+
+    design: "block_frame" -- each 64-key block scaled so that its largest P
+    lands in (128, 256] (the frame attn_fwd_fp8 uses); "plain" -- P =
+    exp(s - max) in (0, 1] rounded as it is; "row_frame" -- one frame per
+    row; "bf16_scores" -- block frame with every score rounded to bf16
+    precision (an accumulation error of one bf16 rounding of the sum).
+    """
     B, H, N, d = inp.q.shape
     sigma = float(np.float32(inp.scale))
     out = np.zeros((B, H, N, d))
@@ -91,17 +109,23 @@ def _sim_fp8(inp, mistake=None):
             q, k, v = inp.q[b, h], inp.k[b, h], inp.v[b, h]
             if mistake == "no_v_descale":
                 v = v / inp.vd
-            s = np.where(vis, sigma * (q @ k.T), -np.inf)
+            s = sigma * (q @ k.T)
+            if design == "bf16_scores":
+                s = _bf16(s)
+            s = np.where(vis, s, -np.inf)
             m = s.max(axis=1)
             m = np.where(np.isfinite(m), m, 0.0)
             e = np.where(vis, np.exp(s - m[:, None]), 0.0)
             pq = np.zeros_like(e)
-            blocks = [(0, N)] if mistake == "row_frame" else [(j0, min(N, j0 + 64)) for j0 in range(0, N, 64)]
-            for j0, j1 in blocks:
-                bm = e[:, j0:j1].max(axis=1)
-                u = np.where(bm > 0, 8 - np.ceil(np.log2(np.where(bm > 0, bm, 1.0))), 0.0)
-                frame = np.exp2(u)[:, None]
-                pq[:, j0:j1] = e4m3_round(np.minimum(e[:, j0:j1] * frame, 448.0))[1] / frame
+            if design == "plain":
+                pq = e4m3_round(e)[1]
+            else:
+                blocks = [(0, N)] if design == "row_frame" else [(j0, min(N, j0 + 64)) for j0 in range(0, N, 64)]
+                for j0, j1 in blocks:
+                    bm = e[:, j0:j1].max(axis=1)
+                    u = np.where(bm > 0, 8 - np.ceil(np.log2(np.where(bm > 0, bm, 1.0))), 0.0)
+                    frame = np.exp2(u)[:, None]
+                    pq[:, j0:j1] = e4m3_round(np.minimum(e[:, j0:j1] * frame, 448.0))[1] / frame
             if mistake == "drop_block":
                 pq[:, 64:128] = 0.0
             lq = pq.sum(axis=1)
@@ -129,41 +153,87 @@ CASES = [
 ]
 
 
+def _bounds(fn, inp, **kw):
+    a = (inp.q, inp.k, inp.v, inp.scale)
+    m = dict(causal=inp.causal, window=inp.window, kv_len=inp.kv_len)
+    bO, sO, bL = fn(*a, **m, **kw)
+    bdet, _, _ = fn(*a, **m, **dict(kw, u_p=0.0))
+    return bO, sO, bdet, bL
+
+
 @pytest.mark.parametrize("case", CASES, ids=str)
-def test_fp8_model_covers_simulated_pipeline(case):
+def test_fp8_gate_covers_every_design_and_rejects_mistakes(case):
+    """The gate (format-derived terms) holds for each legal way of rounding P and for bf16-accurate score
+    accumulation; a dropped key block, a mask off by one and a missing V descale escape it."""
     c = dict(case)
     inp = attn_fp8_inputs(c.pop("B"), c.pop("H"), c.pop("N"), 128, seed=50, **c)
     Oref, _ = attention_ref(inp.q, inp.k, inp.v, inp.scale, causal=inp.causal, window=inp.window, kv_len=inp.kv_len)
-    bO, sO, _ = attention_fp8_error_model(inp.q, inp.k, inp.v, inp.scale, causal=inp.causal, window=inp.window,
-                                          kv_len=inp.kv_len)
-    bdet, _, _ = attention_fp8_error_model(inp.q, inp.k, inp.v, inp.scale, causal=inp.causal, window=inp.window,
-                                           kv_len=inp.kv_len, u_p=0.0)
+    bO, sO, bdet, _ = _bounds(attention_fp8_error_bound, inp)
+    for design in ("block_frame", "plain", "row_frame", "bf16_scores"):
+        assert _check(inp, _sim_fp8(inp, design), bO, sO, bdet, Oref) == (True, True), design
+    for mistake in ("drop_block", "mask_off_by_one", "no_v_descale"):
+        assert _check(inp, _sim_fp8(inp, mistake=mistake), bO, sO, bdet, Oref) != (True, True), mistake
+
+
+@pytest.mark.parametrize("case", CASES, ids=str)
+def test_fp8_diagnostic_model_covers_the_block_frame(case):
+    """The tighter model of the kernel's own frame covers that frame and rejects the same mistakes."""
+    c = dict(case)
+    inp = attn_fp8_inputs(c.pop("B"), c.pop("H"), c.pop("N"), 128, seed=50, **c)
+    Oref, _ = attention_ref(inp.q, inp.k, inp.v, inp.scale, causal=inp.causal, window=inp.window, kv_len=inp.kv_len)
+    bO, sO, bdet, _ = _bounds(attention_fp8_error_model, inp)
     assert _check(inp, _sim_fp8(inp), bO, sO, bdet, Oref) == (True, True)
     for mistake in ("drop_block", "mask_off_by_one", "no_v_descale"):
-        assert _check(inp, _sim_fp8(inp, mistake), bO, sO, bdet, Oref) != (True, True), mistake
+        assert _check(inp, _sim_fp8(inp, mistake=mistake), bO, sO, bdet, Oref) != (True, True), mistake
+    gO = attention_fp8_error_bound(inp.q, inp.k, inp.v, inp.scale, causal=inp.causal, window=inp.window,
+                                   kv_len=inp.kv_len)[0]
+    assert np.all(bO <= gO + 1e-300)  # the diagnostic is never looser than the gate
 
 
-def test_fp8_model_catches_a_row_wide_frame():
-    """A frame per row flushes many small P far below one dominant key (here 1.1 % of the mass); the
-    per-block frame keeps them, and the bound (block maxima) tells the two apart."""
+def _dominant_key_case():
+    """Key 0 beats every other key by 2^17.5; the other 2047 keys carry 1.1 % of the mass."""
     inp = attn_fp8_inputs(1, 1, 2048, 128, seed=51)
     sigma = float(np.float32(inp.scale))
     inp.q[:] = 0.0
     inp.k[:] = 0.0
-    inp.q[0, 0, 0, 0] = 17.5 * np.log(2.0) / sigma  # key 0 beats every other key by 2^17.5
+    inp.q[0, 0, 0, 0] = 17.5 * np.log(2.0) / sigma
     inp.k[0, 0, 0, 0] = 1.0
     inp.v[:] = 1.0
     inp.v[0, 0, 0] = 0.0
+    return inp
+
+
+def test_fp8_frames_on_a_row_dominated_by_one_key():
+    """A row-wide frame (or no frame) flushes the small P: legal under the gate, whose a_p term is what
+    covers it (drop that term and the plain design escapes); the diagnostic model of the block frame tells
+    the two designs apart."""
+    inp = _dominant_key_case()
     Oref, _ = attention_ref(inp.q, inp.k, inp.v, inp.scale)
-    bO, sO, _ = attention_fp8_error_model(inp.q, inp.k, inp.v, inp.scale)
-    bdet, _, _ = attention_fp8_error_model(inp.q, inp.k, inp.v, inp.scale, u_p=0.0)
     assert Oref[0, 0, 0, 0] > 0.01
-    assert _check(inp, _sim_fp8(inp), bO, sO, bdet, Oref)[0]
-    assert not _check(inp, _sim_fp8(inp, "row_frame"), bO, sO, bdet, Oref)[0]
+    gate = _bounds(attention_fp8_error_bound, inp)[:3]
+    for design in ("block_frame", "plain", "row_frame"):
+        assert _check(inp, _sim_fp8(inp, design), *gate, Oref)[0], design
+    no_ap = _bounds(attention_fp8_error_bound, inp, a_p=0.0)[:3]
+    assert not _check(inp, _sim_fp8(inp, "plain"), *no_ap, Oref)[0]
+    diag = _bounds(attention_fp8_error_model, inp)[:3]
+    assert _check(inp, _sim_fp8(inp), *diag, Oref)[0]
+    assert not _check(inp, _sim_fp8(inp, "row_frame"), *diag, Oref)[0]
+
+
+def test_fp8_gate_kappa_covers_bf16_accumulation():
+    """Scores carrying one bf16 rounding stay inside the gate; with kappa at float32 level they escape."""
+    inp = attn_fp8_inputs(1, 1, 512, 128, seed=53, causal=True)
+    Oref, _ = attention_ref(inp.q, inp.k, inp.v, inp.scale, causal=True)
+    o = _sim_fp8(inp, "bf16_scores")
+    gate = _bounds(attention_fp8_error_bound, inp)[:3]
+    assert _check(inp, o, *gate, Oref)[0]
+    tight = _bounds(attention_fp8_error_bound, inp, kappa=2.0 ** -24, u_p=0.0, a_p=0.0)[:3]
+    assert not _check(inp, o, *tight, Oref)[0]
 
 
 def test_fp8_model_zero_for_rows_without_keys():
     inp = attn_fp8_inputs(2, 1, 100, 128, seed=52, causal=True, kv_len=[0, 100])
-    bO, sO, bL = attention_fp8_error_model(inp.q, inp.k, inp.v, inp.scale, causal=True, kv_len=inp.kv_len)
-    assert np.all(bO[0] == 0) and np.all(sO[0] == 0) and np.all(bL[0] == 0)
-    assert np.all(bL[1] > 0)
+    for fn in (attention_fp8_error_bound, attention_fp8_error_model):
+        bO, sO, bL = fn(inp.q, inp.k, inp.v, inp.scale, causal=True, kv_len=inp.kv_len)
+        assert np.all(bO[0] == 0) and np.all(sO[0] == 0) and np.all(bL[0] == 0)
+        assert np.all(bL[1] > 0)

@@ -226,3 +226,33 @@ def test_topk_brute_force_small():
             want.append(best)
             left.remove(best)
         assert idx[0].tolist() == want
+
+
+def _first_max_selection(row, k):
+    """Brute force without sorting: k times, scan the row left to right and take the first element that is
+    maximal among those not yet taken (so equal values go to the lower column first)."""
+    taken = set()
+    out = []
+    for _ in range(k):
+        best = None
+        for c in range(len(row)):
+            if c in taken:
+                continue
+            if best is None or row[c] > row[best]:
+                best = c
+        taken.add(best)
+        out.append(best)
+    return out
+
+
+@pytest.mark.parametrize("cols,k", [(65, 16), (3000, 16), (25000, 5), (4099, 1)])
+def test_topk_wide_rows_with_massive_ties_brute_force(cols, k):
+    """Rows wider than 64 columns (the lexsort path of topk_order) with integer values in [-3, 3], so that
+    hundreds of columns share each value: the order must be the first-maximal selection."""
+    rng = np.random.default_rng([14, cols])
+    x = rng.integers(-3, 4, size=(3, cols)).astype(np.float32)
+    x[2, :] = 0.0  # one row entirely tied
+    x[2, cols // 2] = -1.0
+    _, idx = topk_ref(x, k)
+    for r in range(x.shape[0]):
+        assert idx[r].tolist() == _first_max_selection(x[r].tolist(), k)
