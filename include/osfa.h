@@ -16,6 +16,14 @@
  * synchronization.  attn_last_error() returns a description of the last
  * non-OK status on the calling thread.
  *
+ * Debugging: with OSFA_SYNC_CHECK=1 in the environment (read at every
+ * call), each entry point waits for `stream` after a successful launch and
+ * reports a fault of its own kernels as ATTN_ERR_HIP.  Without it nothing
+ * synchronizes.
+ *
+ * Alignment: LSE and kv_len (where present) must be 4-byte aligned; tensor
+ * arguments as stated per entry point.
+ *
  * Inputs are assumed finite; NaN or Inf inputs propagate.  Outputs must not
  * alias inputs, except x == y in online_softmax_rows.
  *

@@ -84,13 +84,22 @@ def _need_device(*ts) -> None:
             raise ValueError("tensors must be contiguous device tensors")
 
 
+def _need_out(t, shape, dtype, like, name: str) -> None:
+    """A caller-supplied output must match exactly: the C ABI cannot see sizes, so a short or mistyped buffer
+    would be written past its end."""
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != like.device:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {like.device} "
+                         f"(got {t.dtype} {tuple(t.shape)} on {t.device})")
+
+
 _DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
 
 def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0,
              kv_len=None, out=None, lse=None, stream=None):
     """O, LSE = attention(q, k, v) for [B, H, N, d] tensors (f32 or bf16)."""
-    _need_device(q, k, v, kv_len, out, lse)
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -98,12 +107,15 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, window: 
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _need_out(out, q.shape, q.dtype, q, "out")
+    _need_out(lse, (B, H, N), torch.float32, q, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B):
-        raise ValueError("kv_len must be int32 [B]")
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B or kv_len.device != q.device):
+        raise ValueError("kv_len must be int32 [B] on the device of q")
+    _need_device(q, k, v, kv_len, out, lse)
     _check(load_library().attn_fwd(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                                    float(scale), int(bool(causal)), int(window), _ptr(kv_len), _stream(stream)))
     return out, lse
@@ -112,7 +124,6 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, window: 
 def attn_fwd_exp2_offload(q, k, v, poly_every: int, scale: float | None = None, causal: bool = False,
                           window: int = 0, kv_len=None, out=None, lse=None, stream=None):
     """attn_fwd for bf16 [B, H, N, 128] with one exponential in poly_every (2, 4, 8) on the FMA pipes."""
-    _need_device(q, k, v, kv_len, out, lse)
     if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must be bfloat16")
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -120,12 +131,15 @@ def attn_fwd_exp2_offload(q, k, v, poly_every: int, scale: float | None = None, 
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _need_out(out, q.shape, q.dtype, q, "out")
+    _need_out(lse, (B, H, N), torch.float32, q, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B):
-        raise ValueError("kv_len must be int32 [B]")
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B or kv_len.device != q.device):
+        raise ValueError("kv_len must be int32 [B] on the device of q")
+    _need_device(q, k, v, kv_len, out, lse)
     _check(load_library().attn_fwd_exp2_offload(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                                                 float(scale), int(bool(causal)), int(window), _ptr(kv_len),
                                                 int(poly_every), _stream(stream)))
@@ -135,7 +149,6 @@ def attn_fwd_exp2_offload(q, k, v, poly_every: int, scale: float | None = None, 
 def attn_fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, scale: float | None = None,
                  causal: bool = False, window: int = 0, kv_len=None, out=None, lse=None, stream=None):
     """O (bf16), LSE = attention of e4m3 codes q, k, v ([B, H, N, d], uint8 or float8_e4m3fn) x their descales."""
-    _need_device(q, k, v, kv_len, out, lse)
     ok = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
     if q.dtype not in ok or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype uint8 or float8_e4m3fn (e4m3 codes)")
@@ -144,14 +157,15 @@ def attn_fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, 
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _need_out(out, q.shape, torch.bfloat16, q, "out")
+    _need_out(lse, (B, H, N), torch.float32, q, "lse")
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
-    if out.dtype != torch.bfloat16 or out.shape != q.shape:
-        raise ValueError("out must be bf16 [B, H, N, d]")
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B):
-        raise ValueError("kv_len must be int32 [B]")
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B or kv_len.device != q.device):
+        raise ValueError("kv_len must be int32 [B] on the device of q")
+    _need_device(q, k, v, kv_len, out, lse)
     _check(load_library().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                                        float(q_descale), float(k_descale), float(v_descale), int(bool(causal)),
                                        int(window), _ptr(kv_len), _stream(stream)))
@@ -165,7 +179,6 @@ def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
 def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False, window: int = 0,
              kv_len=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """(dQ, dK, dV) of attention for [B, H, N, d] bf16 tensors, given O and LSE from attn_fwd."""
-    _need_device(q, k, v, o, dout, lse, kv_len, dq, dk, dv, workspace)
     if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, o, dout)):
         raise ValueError("q, k, v, o, dout must share one dtype")
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
@@ -173,16 +186,22 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = F
     B, H, N, d = q.shape
     if lse.dtype != torch.float32 or lse.shape != (B, H, N):
         raise ValueError("lse must be float32 [B, H, N]")
-    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B):
-        raise ValueError("kv_len must be int32 [B]")
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != B or kv_len.device != q.device):
+        raise ValueError("kv_len must be int32 [B] on the device of q")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need_out(t, q.shape, q.dtype, q, name)
+    if workspace is not None and (workspace.device != q.device or
+                                  workspace.numel() * workspace.element_size() < bwd_workspace_bytes(B, H, N)):
+        raise ValueError("workspace must be on the device of q and hold bwd_workspace_bytes(B, H, N) bytes")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     need = bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    _need_device(q, k, v, o, dout, lse, kv_len, dq, dk, dv, workspace)
     _check(load_library().attn_bwd(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                                    int(window), _ptr(kv_len), _ptr(workspace),
@@ -196,17 +215,20 @@ def decode_workspace_bytes(B: int, H: int, d: int, nsplit: int) -> int:
 
 def attn_decode_splitkv(q, k, v, nsplit: int, out=None, workspace=None, stream=None):
     """o [B, H, d] float32 from q [B, H, d] and K, V [B, H, Nkv, d]."""
-    _need_device(q, k, v, out, workspace)
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
     B, H, Nkv, d = k.shape
     if q.shape != (B, H, d) or v.shape != k.shape:
         raise ValueError("q must be [B, H, d] and K, V [B, H, Nkv, d]")
+    _need_out(out, (B, H, d), torch.float32, q, "out")
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError("workspace must be on the device of q")
     if out is None:
         out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
     need = decode_workspace_bytes(B, H, d, nsplit)
     if workspace is None:
         workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    _need_device(q, k, v, out, workspace)
     _check(load_library().attn_decode_splitkv(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Nkv, d,
                                               int(nsplit), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                               _stream(stream)))
@@ -215,25 +237,26 @@ def attn_decode_splitkv(q, k, v, nsplit: int, out=None, workspace=None, stream=N
 
 def online_softmax_rows(x, out=None, stream=None):
     """y = softmax(x, dim=-1) for a 2-D float32 tensor."""
-    _need_device(x, out)
     if x.dtype != torch.float32 or x.dim() != 2:
         raise ValueError("x must be a 2-D float32 tensor")
+    _need_out(out, x.shape, torch.float32, x, "out")
     if out is None:
         out = torch.empty_like(x)
     rows, cols = x.shape
+    _need_device(x, out)
     _check(load_library().online_softmax_rows(_ptr(x), _ptr(out), rows, cols, _stream(stream)))
     return out
 
 
 def online_softmax_topk_rows(x, k: int, with_probs: bool = False, stream=None):
     """(topv [rows, k] float32, topi [rows, k] int32[, y]) of softmax(x) per row."""
-    _need_device(x)
     if x.dtype != torch.float32 or x.dim() != 2:
         raise ValueError("x must be a 2-D float32 tensor")
     rows, cols = x.shape
     topv = torch.empty((rows, k), dtype=torch.float32, device=x.device)
     topi = torch.empty((rows, k), dtype=torch.int32, device=x.device)
     y = torch.empty_like(x) if with_probs else None
+    _need_device(x)
     _check(load_library().online_softmax_topk_rows(_ptr(x), _ptr(y), _ptr(topv), _ptr(topi), rows, cols, int(k),
                                                    _stream(stream)))
     return (topv, topi, y) if with_probs else (topv, topi)

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "launch.h"
@@ -21,10 +22,26 @@ attn_status_t fail(attn_status_t st, const char* fmt, ...) {
   return st;
 }
 
-attn_status_t hip_status(hipError_t e, const char* what) {
-  if (e == hipSuccess) return ATTN_OK;
-  return fail(ATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+// OSFA_SYNC_CHECK=1 in the environment (read at every call): after a
+// successful launch, wait for the stream and report a fault of the kernel
+// as ATTN_ERR_HIP from the call that launched it.  A debugging aid; without
+// it the library never synchronizes.
+bool sync_check() {
+  const char* v = std::getenv("OSFA_SYNC_CHECK");
+  return v && v[0] == '1' && v[1] == '\0';
 }
+
+attn_status_t hip_status(hipError_t e, const char* what, hipStream_t stream) {
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  if (sync_check()) {
+    const hipError_t s = hipStreamSynchronize(stream);
+    if (s != hipSuccess) return fail(ATTN_ERR_HIP, "%s: kernel failed (OSFA_SYNC_CHECK): %s", what, hipGetErrorString(s));
+  }
+  return ATTN_OK;
+}
+
+// LSE is float32 and kv_len int32: both must be 4-byte aligned (kv_len may be NULL).
+bool misaligned4(const void* a, const void* b) { return (((uintptr_t)a | (uintptr_t)b) & 3) != 0; }
 
 constexpr long long kMaxElems = 1LL << 40;
 
@@ -53,9 +70,10 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* Q, const void* K, const v
   if (window < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: window must be >= 0 (0 = no window)");
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
     return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: Q, K, V, O must be 16-byte aligned");
+  if (misaligned4(LSE, kv_len)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd: LSE and kv_len must be 4-byte aligned");
   osfa::FwdArgs a{Q, K, V, O, LSE, kv_len, B, H, N, d, scale, causal, window};
   const hipError_t e = dtype == ATTN_BF16 ? osfa::launch_attn_fwd_bf16(a, stream) : osfa::launch_attn_fwd_f32(a, stream);
-  return hip_status(e, "attn_fwd");
+  return hip_status(e, "attn_fwd", stream);
 }
 
 attn_status_t attn_fwd_exp2_offload(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
@@ -77,8 +95,9 @@ attn_status_t attn_fwd_exp2_offload(const void* Q, const void* K, const void* V,
   if (window < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: window must be >= 0 (0 = no window)");
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
     return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: Q, K, V, O must be 16-byte aligned");
+  if (misaligned4(LSE, kv_len)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_exp2_offload: LSE and kv_len must be 4-byte aligned");
   osfa::FwdArgs a{Q, K, V, O, LSE, kv_len, B, H, N, d, scale, causal, window};
-  return hip_status(osfa::launch_attn_fwd_bf16_exp2_offload(a, poly_every, stream), "attn_fwd_exp2_offload");
+  return hip_status(osfa::launch_attn_fwd_bf16_exp2_offload(a, poly_every, stream), "attn_fwd_exp2_offload", stream);
 }
 
 attn_status_t attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
@@ -102,8 +121,9 @@ attn_status_t attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O,
   if (window < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: window must be >= 0 (0 = no window)");
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
     return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: Q, K, V, O must be 16-byte aligned");
+  if (misaligned4(LSE, kv_len)) return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_fp8: LSE and kv_len must be 4-byte aligned");
   osfa::FwdArgs a{Q, K, V, O, LSE, kv_len, B, H, N, d, scale, causal, window};
-  return hip_status(osfa::launch_attn_fwd_fp8(a, qk, v_descale, stream), "attn_fwd_fp8");
+  return hip_status(osfa::launch_attn_fwd_fp8(a, qk, v_descale, stream), "attn_fwd_fp8", stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N) {
@@ -135,10 +155,10 @@ attn_status_t attn_bwd(attn_dtype_t dtype, const void* Q, const void* K, const v
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK |
        (uintptr_t)dV) & 15)
     return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned");
-  if (((uintptr_t)LSE | (uintptr_t)workspace) & 3)
-    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: LSE and workspace must be 4-byte aligned");
+  if (((uintptr_t)LSE | (uintptr_t)workspace | (uintptr_t)kv_len) & 3)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: LSE, workspace and kv_len must be 4-byte aligned");
   osfa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, kv_len, static_cast<float*>(workspace), B, H, N, d, scale, causal, window};
-  return hip_status(osfa::launch_attn_bwd_bf16(a, stream), "attn_bwd");
+  return hip_status(osfa::launch_attn_bwd_bf16(a, stream), "attn_bwd", stream);
 }
 
 size_t attn_decode_splitkv_workspace_bytes(int B, int H, int d, int nsplit) {
@@ -168,7 +188,7 @@ attn_status_t attn_decode_splitkv(attn_dtype_t dtype, const void* q, const void*
     return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv: o and workspace must be 4-byte aligned");
   osfa::DecodeArgs a{q, K, V, o, static_cast<float*>(workspace), B, H, Nkv, d, nsplit};
   const hipError_t e = dtype == ATTN_BF16 ? osfa::launch_decode_bf16(a, stream) : osfa::launch_decode_f32(a, stream);
-  return hip_status(e, "attn_decode_splitkv");
+  return hip_status(e, "attn_decode_splitkv", stream);
 }
 
 attn_status_t online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream) {
@@ -183,7 +203,7 @@ attn_status_t online_softmax_rows(const float* x, float* y, int rows, int cols, 
     if (xb < yb + bytes && yb < xb + bytes)
       return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: x and y overlap partially");
   }
-  return hip_status(osfa::launch_softmax_rows(x, y, rows, cols, stream), "online_softmax_rows");
+  return hip_status(osfa::launch_softmax_rows(x, y, rows, cols, stream), "online_softmax_rows", stream);
 }
 
 attn_status_t online_softmax_topk_rows(const float* x, float* y, float* topv, int32_t* topi, int rows, int cols, int k,
@@ -196,7 +216,7 @@ attn_status_t online_softmax_topk_rows(const float* x, float* y, float* topv, in
   if (((uintptr_t)x | (uintptr_t)topv | (uintptr_t)topi | (uintptr_t)y) & 3)
     return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: pointers must be 4-byte aligned");
   if (y == x) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_topk_rows: y must not alias x");
-  return hip_status(osfa::launch_softmax_topk(x, y, topv, topi, rows, cols, k, stream), "online_softmax_topk_rows");
+  return hip_status(osfa::launch_softmax_topk(x, y, topv, topi, rows, cols, k, stream), "online_softmax_topk_rows", stream);
 }
 
 }  // extern "C"

@@ -2,7 +2,7 @@
 // translation units.  Arguments reaching a launcher have been validated.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 

@@ -1,8 +1,10 @@
 """CPU tests of the C-ABI library: it loads, exports every declared symbol,
 and rejects invalid arguments on the host before any launch.
 
-No call here reaches a kernel launch: every call fails validation first
-(the fake pointers are never dereferenced).
+Calls with invalid arguments fail validation before any launch (the fake
+pointers are never dereferenced).  The only valid calls are in
+``test_valid_call_without_a_device_reports_hip_error``, which runs only where
+no GPU is visible: there the launch itself is refused by the runtime.
 """
 import ctypes
 import os
@@ -77,6 +79,8 @@ def _fwd(lib, **kw):
     (dict(Q=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "aligned"),
     (dict(B=1 << 12, H=1 << 12, N=1 << 12, d=128), bd.ATTN_ERR_INVALID_ARG, "too large"),
     (dict(N=1 << 23, d=128), bd.ATTN_ERR_INVALID_ARG, "one head"),
+    (dict(LSE=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "LSE and kv_len"),
+    (dict(kv_len=FAKE + 1), bd.ATTN_ERR_INVALID_ARG, "LSE and kv_len"),
 ])
 def test_attn_fwd_rejects(lib, kw, status, msg):
     assert _fwd(lib, **kw) == status
@@ -103,6 +107,8 @@ def _exp2_offload(lib, **kw):
     (dict(window=-1), bd.ATTN_ERR_INVALID_ARG, "window"),
     (dict(O=FAKE + 8), bd.ATTN_ERR_INVALID_ARG, "aligned"),
     (dict(N=1 << 23), bd.ATTN_ERR_INVALID_ARG, "one head"),
+    (dict(LSE=FAKE + 1), bd.ATTN_ERR_INVALID_ARG, "LSE and kv_len"),
+    (dict(kv_len=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "LSE and kv_len"),
 ])
 def test_exp2_offload_rejects(lib, kw, status, msg):
     assert _exp2_offload(lib, **kw) == status
@@ -161,6 +167,8 @@ def _fp8(lib, **kw):
     (dict(window=-1), bd.ATTN_ERR_INVALID_ARG, "window"),
     (dict(O=FAKE + 4), bd.ATTN_ERR_INVALID_ARG, "aligned"),
     (dict(N=1 << 23), bd.ATTN_ERR_INVALID_ARG, "one head"),
+    (dict(LSE=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "LSE and kv_len"),
+    (dict(kv_len=FAKE + 3), bd.ATTN_ERR_INVALID_ARG, "LSE and kv_len"),
 ])
 def test_fp8_rejects(lib, kw, status, msg):
     assert _fp8(lib, **kw) == status
@@ -189,6 +197,7 @@ def _bwd(lib, **kw):
     (dict(ws_bytes=2 * 2 * 16 * 4 - 1), bd.ATTN_ERR_INVALID_ARG, "workspace"),
     (dict(dK=FAKE + 8), bd.ATTN_ERR_INVALID_ARG, "aligned"),
     (dict(LSE=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(kv_len=FAKE + 2), bd.ATTN_ERR_INVALID_ARG, "aligned"),
     (dict(N=1 << 23), bd.ATTN_ERR_INVALID_ARG, "one head"),
 ])
 def test_bwd_rejects(lib, kw, status, msg):
@@ -263,3 +272,74 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     x = torch.zeros(4, 8)
     with pytest.raises((RuntimeError, ValueError)):
         osfa.online_softmax_rows(x)
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="valid calls with fake pointers must never reach a real device")
+def test_valid_call_without_a_device_reports_hip_error(lib):
+    """Valid arguments and no device: every entry point returns ATTN_ERR_HIP (the runtime refuses the launch),
+    never crashes and never reports success."""
+    calls = {
+        "attn_fwd": lambda: _fwd(lib),
+        "attn_fwd_exp2_offload": lambda: _exp2_offload(lib),
+        "attn_fwd_fp8": lambda: _fp8(lib),
+        "attn_bwd": lambda: _bwd(lib),
+        "attn_decode_splitkv": lambda: _dec(lib),
+        "online_softmax_rows": lambda: lib.online_softmax_rows(FAKE, FAKE, 4, 100, None),
+        "online_softmax_topk_rows": lambda: lib.online_softmax_topk_rows(FAKE, None, FAKE * 2, FAKE * 3, 4, 100, 5,
+                                                                         None),
+    }
+    for name, call in calls.items():
+        assert call() == bd.ATTN_ERR_HIP, name
+        text = lib.attn_last_error().decode()
+        assert name in text and "launch failed" in text, text
+
+
+def _cpu(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("which", ["out_dtype", "out_shape", "lse_shape", "lse_dtype"])
+def test_binding_checks_supplied_outputs_before_any_launch(which):
+    """A caller-supplied output of the wrong dtype or shape raises ValueError before the library is called
+    (the ABI cannot see buffer sizes: a short buffer would be written past its end)."""
+    import torch
+    q = _cpu((1, 2, 16, 128), torch.bfloat16)
+    out, lse = _cpu((1, 2, 16, 128), torch.bfloat16), _cpu((1, 2, 16), torch.float32)
+    if which == "out_dtype":
+        out = _cpu((1, 2, 16, 128), torch.float32)
+    elif which == "out_shape":
+        out = _cpu((1, 2, 15, 128), torch.bfloat16)
+    elif which == "lse_shape":
+        lse = _cpu((1, 2, 8), torch.float32)
+    else:
+        lse = _cpu((1, 2, 16), torch.bfloat16)
+    name = "out" if which.startswith("out") else "lse"
+    for fn in (lambda: bd.attn_fwd(q, q, q, out=out, lse=lse),
+               lambda: bd.attn_fwd_exp2_offload(q, q, q, 4, out=out, lse=lse)):
+        with pytest.raises(ValueError, match=f"^{name} must be"):
+            fn()
+
+
+def test_binding_checks_other_supplied_outputs():
+    import torch
+    q = _cpu((1, 2, 16, 128), torch.bfloat16)
+    lse = _cpu((1, 2, 16), torch.float32)
+    with pytest.raises(ValueError, match="^dk must be"):
+        bd.attn_bwd(q, q, q, q, q, lse, dk=_cpu((1, 2, 16, 128), torch.float32))
+    u8 = _cpu((1, 2, 16, 128), torch.uint8)
+    with pytest.raises(ValueError, match="^out must be"):
+        bd.attn_fwd_fp8(u8, u8, u8, 1.0, 1.0, 1.0, out=_cpu((1, 2, 16, 128), torch.float32))
+    with pytest.raises(ValueError, match="^out must be"):
+        bd.attn_decode_splitkv(_cpu((1, 2, 128), torch.bfloat16), q, q, 4, out=_cpu((1, 2, 128), torch.bfloat16))
+    x = _cpu((4, 100), torch.float32)
+    with pytest.raises(ValueError, match="^out must be"):
+        bd.online_softmax_rows(x, out=_cpu((4, 99), torch.float32))
