@@ -3,6 +3,10 @@
 One step runs every kernel of the path once, each on its own workload:
   * attn_fwd, bf16, B=1, H=64, N=8192, d=128, causal, sliding window 1024,
     last 512 keys padded, 1 % of keys scaled by 8  (the headline workload);
+  * attn_fwd, bf16, B=4, H=32, N=2048, d=128, causal (reported under
+    `kernels`, with its fraction of the bf16 peak);
+  * attn_fwd, float32, B=1, H=1, N=1000, d=64, no mask (reported under
+    `kernels` in microseconds: far too small to fill the chip);
   * attn_decode_splitkv, bf16, 32 heads, 131072 keys, d=128, 64 splits;
   * online_softmax_rows, float32, 4096 x 4000;
   * online_softmax_topk_rows, float32, 1024 x 25000, k=5;
@@ -19,8 +23,10 @@ forward pass's algorithmic TFLOP/s (4 d FLOPs per visible query-key pair)
 over its average launch time.  Within a step the 2 GiB decode stream
 evicts the softmax inputs from the caches, so those kernels read from HBM.
 
-The `cpu_baseline` leg times the FP64 CPU oracle on a bounded sample of the
-forward workload (whole heads, about 15 s of CPU work) on this host.
+The `cpu_baseline` leg times the FP64 CPU oracle on this host: its top-level
+figure on a bounded sample of the headline forward workload (whole heads),
+and under `per_config` on a bounded sample of every other workload (whole
+heads, rows or queries), about 25 s of CPU work in all.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line.
@@ -41,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU-oracle sample budget for the headline workload (each other workload gets a share)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -103,6 +110,22 @@ def main():
     po = torch.empty_like(fo)
     plse = torch.empty_like(flse)
 
+    # --- causal 2048 workload and the float32 N = 1000 workload ------------------
+    c3_name = "attn_bf16_causal_b4h32_n2048_d128"
+    c3 = WORKLOADS[c3_name]
+    c3in = workload_attn_inputs(c3_name)
+    c3q, c3k, c3v = up_bf16(c3in.q_bits), up_bf16(c3in.k_bits), up_bf16(c3in.v_bits)
+    c3o = torch.empty_like(c3q)
+    c3lse = torch.empty((c3["B"], c3["H"], c3["N"]), dtype=torch.float32, device=dev)
+    c3_flops = acc.attn_flops(c3["B"], c3["H"], c3["N"], c3["d"], c3["causal"], c3["window"], None)
+    c1_name = "attn_f32_b1h1_n1000_d64"
+    c1 = WORKLOADS[c1_name]
+    c1in = workload_attn_inputs(c1_name)
+    c1q, c1k, c1v = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (c1in.q, c1in.k, c1in.v))
+    c1o = torch.empty_like(c1q)
+    c1lse = torch.empty((c1["B"], c1["H"], c1["N"]), dtype=torch.float32, device=dev)
+    c1_flops = acc.attn_flops(c1["B"], c1["H"], c1["N"], c1["d"], c1["causal"], c1["window"], None)
+
     # --- decode workload --------------------------------------------------------
     dw_name = "decode_bf16_b1h32_nkv131072_d128_split64"
     dw = WORKLOADS[dw_name]
@@ -163,6 +186,12 @@ def main():
                                                 bdv.data_ptr(), fw["B"], fw["H"], fw["N"], fw["d"], fin.scale, 1,
                                                 fw["window"], fkv.data_ptr(), bws.data_ptr(), bws.numel() * 4,
                                                 sh))),
+        ("attn_fwd_causal_2048", lambda: check(lib.attn_fwd(1, c3q.data_ptr(), c3k.data_ptr(), c3v.data_ptr(),
+                                                            c3o.data_ptr(), c3lse.data_ptr(), c3["B"], c3["H"],
+                                                            c3["N"], c3["d"], c3in.scale, 1, 0, None, sh))),
+        ("attn_fwd_f32_n1000", lambda: check(lib.attn_fwd(0, c1q.data_ptr(), c1k.data_ptr(), c1v.data_ptr(),
+                                                          c1o.data_ptr(), c1lse.data_ptr(), c1["B"], c1["H"],
+                                                          c1["N"], c1["d"], c1in.scale, 0, 0, None, sh))),
     ]
 
     def step(events=None):
@@ -200,8 +229,11 @@ def main():
     bwd_tflops = bw_flops / (ms["attn_bwd"] * 1e-3) / 1e12
     f8_tflops = fw_flops / (ms["attn_fwd_fp8"] * 1e-3) / 1e12
     px_tflops = fw_flops / (ms["attn_fwd_exp2_offload"] * 1e-3) / 1e12
+    c3_tflops = c3_flops / (ms["attn_fwd_causal_2048"] * 1e-3) / 1e12
+    c1_tflops = c1_flops / (ms["attn_fwd_f32_n1000"] * 1e-3) / 1e12
 
     cpu = cpu_baseline(fin, fw, args.cpu_seconds)
+    cpu["per_config"] = cpu_baseline_per_config(args.cpu_seconds, c1in, c3in, sx, tx, dw)
 
     # Measured HBM bytes per launch (rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE,
     # scaled by a 1 GiB copy), recorded under profiles/ together with a hash
@@ -266,6 +298,15 @@ def main():
                                       "min_us": round(ms_min["attn_fwd_exp2_offload"] * 1e3, 2),
                                       "tflops": round(px_tflops, 2),
                                       "frac_mfma_peak": round(px_tflops / acc.PEAK_BF16_TFLOPS, 4)},
+            "attn_fwd_causal_2048": {"workload": c3_name, "avg_us": round(ms["attn_fwd_causal_2048"] * 1e3, 2),
+                                     "min_us": round(ms_min["attn_fwd_causal_2048"] * 1e3, 2),
+                                     "tflops": round(c3_tflops, 2),
+                                     "frac_mfma_peak": round(c3_tflops / acc.PEAK_BF16_TFLOPS, 4),
+                                     "algorithmic_flop": c3_flops},
+            "attn_fwd_f32_n1000": {"workload": c1_name, "avg_us": round(ms["attn_fwd_f32_n1000"] * 1e3, 2),
+                                   "min_us": round(ms_min["attn_fwd_f32_n1000"] * 1e3, 2),
+                                   "tflops": round(c1_tflops, 3), "algorithmic_flop": c1_flops,
+                                   "bound": "latency (one head of 1000 queries: 8 query tiles)"},
             "attn_bwd": {"workload": fw_name, "avg_us": round(ms["attn_bwd"] * 1e3, 2),
                          "min_us": round(ms_min["attn_bwd"] * 1e3, 2), "tflops": round(bwd_tflops, 2),
                          "frac_mfma_peak": round(bwd_tflops / acc.PEAK_BF16_TFLOPS, 4),
@@ -277,16 +318,20 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(fin, fw, budget_s: float):
     """Time the FP64 oracle on whole heads of the forward workload until the budget is spent."""
     from online_softmax_fa2_amd import accounting as acc
     from oracle import attention_ref
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     done = 0
     t0 = time.perf_counter()
     while done < fw["H"]:
@@ -301,6 +346,69 @@ def cpu_baseline(fin, fw, budget_s: float):
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {fw['H']} heads of the forward workload (all 8192 queries each), "
                       f"FP64 NumPy oracle, {el:.1f} s"}
+
+
+def cpu_baseline_per_config(budget_s: float, c1in, c3in, sx, tx, dw):
+    """The FP64 oracle on a bounded sample of each other workload: whole heads (attention, decode) or whole
+    rows (softmax, top-k), taken until a share of the budget is spent, scaled to the GPU metric's unit."""
+    from online_softmax_fa2_amd import accounting as acc
+    from online_softmax_fa2_amd.inputs import decode_slice
+    from oracle import attention_ref, decode_ref, softmax_ref, topk_ref
+
+    threads = _blas_threads()
+    share = budget_s / 4.0
+    out = {}
+
+    def timed(units, run_one):
+        done, t0 = 0, time.perf_counter()
+        while done < units:
+            run_one(done)
+            done += 1
+            if time.perf_counter() - t0 >= share:
+                break
+        return done, time.perf_counter() - t0
+
+    # float32 attention, one head of 1000 queries: the whole workload, several times if it is quick.
+    reps, el = timed(50, lambda _: attention_ref(c1in.q, c1in.k, c1in.v, c1in.scale))
+    out["attn_f32_b1h1_n1000_d64"] = {"value": round(el / reps * 1e6, 1), "unit": "us", "cores": threads,
+                                      "kind": "oracle", "sample": f"the whole workload, {reps} runs"}
+    # bf16 causal 4 x 32 x 2048: whole heads.
+    B, H, N, d = c3in.q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    n, el = timed(len(heads), lambda i: attention_ref(
+        c3in.q[heads[i][0]:heads[i][0] + 1, heads[i][1]:heads[i][1] + 1],
+        c3in.k[heads[i][0]:heads[i][0] + 1, heads[i][1]:heads[i][1] + 1],
+        c3in.v[heads[i][0]:heads[i][0] + 1, heads[i][1]:heads[i][1] + 1], c3in.scale, causal=True))
+    fl = acc.attn_flops(1, n, N, d, True, 0, None)
+    out["attn_bf16_causal_b4h32_n2048_d128"] = {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s",
+                                                "cores": threads, "kind": "oracle",
+                                                "sample": f"{n} of {len(heads)} heads, {el:.1f} s"}
+    # row softmax and the fused top-5: blocks of 64 whole rows.
+    xs = sx.cpu().numpy()
+    n, el = timed(xs.shape[0] // 64, lambda i: softmax_ref(xs[64 * i:64 * i + 64]))
+    out["softmax_rows_4096x4000"] = {"value": round(acc.softmax_bytes(64 * n, xs.shape[1]) / el / 1e9, 3),
+                                     "unit": "GB/s", "cores": threads, "kind": "oracle",
+                                     "sample": f"{64 * n} of {xs.shape[0]} rows, {el:.1f} s"}
+    xt = tx.cpu().numpy()
+    n, el = timed(xt.shape[0] // 16, lambda i: topk_ref(xt[16 * i:16 * i + 16], 5))
+    out["softmax_top5_1024x25000"] = {"value": round(acc.topk_bytes(16 * n, xt.shape[1], 5) / el / 1e9, 3),
+                                      "unit": "GB/s", "cores": threads, "kind": "oracle",
+                                      "sample": f"{16 * n} of {xt.shape[0]} rows, {el:.1f} s"}
+    # split-KV decode: whole heads (the oracle needs no split).
+    def dec(h):
+        q, k, v, _, _, _ = decode_slice(dw["seed"], 0, h, dw["Nkv"], dw["d"])
+        t = time.perf_counter()
+        decode_ref(q[None, None], k[None, None], v[None, None])
+        return time.perf_counter() - t
+    spent, n, t0 = 0.0, 0, time.perf_counter()
+    while n < dw["H"] and time.perf_counter() - t0 < share:  # the budget covers input generation too
+        spent += dec(n)
+        n += 1
+    out["decode_bf16_b1h32_nkv131072_d128_split64"] = {
+        "value": round(acc.decode_bytes(1, n, dw["Nkv"], dw["d"]) / spent / 1e9, 3), "unit": "GB/s",
+        "cores": threads, "kind": "oracle",
+        "sample": f"{n} of {dw['H']} heads (input generation not timed), {spent:.1f} s"}
+    return out
 
 
 if __name__ == "__main__":

@@ -16,6 +16,8 @@ Tolerances (the bar the tests apply):
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -106,3 +108,9 @@ def assert_lse_abs(got, ref, tol=1e-3, what=""):
     assert np.array_equal(np.isinf(got), inf) and np.all(got[inf] == ref[inf]), f"{what}: -inf rows differ"
     err = np.abs(got[~inf] - ref[~inf])
     assert err.size == 0 or err.max() <= tol, f"{what}: LSE max abs err {err.max():.3e} > {tol}"
+
+
+def oracle_map(fn, items, workers: int = 8):
+    """[fn(x) for x in items], run on a thread pool (NumPy releases the GIL in its array kernels)."""
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))

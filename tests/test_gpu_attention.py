@@ -1,9 +1,9 @@
 """GPU parity: attn_fwd (float32 and bfloat16) against the FP64 oracle.
 
 Small cases span several 128-query tiles and 64-key blocks with ragged
-tails, every mask combination, fully masked rows and late maxima; the full
-workloads are checked on whole heads plus rows sampled across all heads,
-in the launch configuration the benchmark times.
+tails and exact multiples of the block sizes, every mask combination, fully
+masked rows and late maxima; the full workloads are checked element by
+element on every head, in the launch configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -12,8 +12,8 @@ import torch
 import online_softmax_fa2_amd as osfa
 from online_softmax_fa2_amd.inputs import WORKLOADS, attn_bits_large, attn_inputs, bf16_bits_to_f32, workload_attn_inputs
 from oracle import attention_ref
-from tests.gpu_util import (Guarded, assert_bf16_out, assert_f32_rel, assert_lse_abs, assert_normwise, upload_bf16,
-                            upload_f32)
+from tests.gpu_util import (Guarded, assert_bf16_out, assert_f32_rel, assert_lse_abs, assert_normwise, oracle_map,
+                            upload_bf16, upload_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,13 +43,18 @@ def run_fwd(inp, poly_every=0):
 
 
 def check(inp, O, L, rows=None, heads=None):
-    """Compare (selected heads / rows of) the GPU result with the oracle."""
+    """Compare (selected heads / rows of) the GPU result with the oracle, element by element."""
     B, H, N, d = inp.q.shape
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
-    for b, h in heads:
+
+    def ref(bh):
+        b, h = bh
         sl = (slice(b, b + 1), slice(h, h + 1))
-        Or, Lr = attention_ref(inp.q[sl], inp.k[sl], inp.v[sl], inp.scale, causal=inp.causal, window=inp.window,
-                               kv_len=None if inp.kv_len is None else inp.kv_len[b:b + 1], rows=rows)
+        return attention_ref(inp.q[sl], inp.k[sl], inp.v[sl], inp.scale, causal=inp.causal, window=inp.window,
+                             kv_len=None if inp.kv_len is None else inp.kv_len[b:b + 1], rows=rows)
+
+    refs = oracle_map(ref, heads) if len(heads) > 1 else [ref(heads[0])]
+    for (b, h), (Or, Lr) in zip(heads, refs):
         og = O[b, h] if rows is None else O[b, h, rows]
         lg = L[b, h] if rows is None else L[b, h, rows]
         what = f"b={b} h={h}"
@@ -79,6 +84,16 @@ CASES = [
     (3, 2, 127, 128, False, 1000, None, 0),
     (1, 1, 200, 64, False, 2**31 - 1, None, 0),   # window beyond N: no mask
     (2, 1, 150, 128, True, 2**31 - 1, [150, 77], 0),
+    # exact multiples of the tile (128) and block (64) sizes, and one short of them
+    (1, 2, 2, 128, True, 0, None, 0),
+    (1, 2, 63, 128, False, 0, None, 0),
+    (1, 2, 64, 64, True, 0, None, 0),
+    (1, 2, 128, 128, True, 0, None, 0),
+    (2, 1, 256, 64, False, 0, [256, 192], 0),
+    (1, 1, 512, 128, True, 0, [448], 2),
+    # the benchmark's window of 1024 at a size the oracle finishes quickly
+    (1, 2, 1600, 128, True, 1024, [1400], 3),
+    (1, 1, 2048, 64, True, 1024, None, 0),
 ]
 
 
@@ -128,18 +143,21 @@ def test_fwd_closed_forms_bf16():
     assert np.all(O == 1.0)
 
 
-def _full(name, heads, nrows=64, poly_every=0):
+def _full(name, heads=None, nrows=64, poly_every=0):
+    """The full workload; heads=None compares every head whole, otherwise the listed heads whole plus sampled
+    rows of every fifth head."""
     w = WORKLOADS[name]
     print(f"attn_fwd full workload {name} poly_every={poly_every}", flush=True)
     inp = workload_attn_inputs(name)
     O, L = run_fwd(inp, poly_every)
     assert not np.isnan(O).any() and not np.isnan(L).any()
     check(inp, O, L, heads=heads)
-    rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(w["N"], nrows, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, w["N"] - 1]]))
-    all_heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
-    check(inp, O, L, rows=rows, heads=all_heads[::5])
+    if heads is not None:
+        rng = np.random.default_rng(123)
+        rows = np.sort(rng.choice(w["N"], nrows, replace=False))
+        rows = np.unique(np.concatenate([rows, [0, w["N"] - 1]]))
+        all_heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
+        check(inp, O, L, rows=rows, heads=all_heads[::5])
     return inp, O, L
 
 
@@ -181,11 +199,13 @@ def test_fwd_full_f32_n1000():
 
 
 def test_fwd_full_bf16_causal_2048():
-    _full("attn_bf16_causal_b4h32_n2048_d128", heads=[(0, 0), (1, 7), (3, 31)])
+    """All 128 heads of the causal 4 x 32 x 2048 workload, element by element."""
+    _full("attn_bf16_causal_b4h32_n2048_d128")
 
 
 def test_fwd_full_bf16_window_pad_8192():
-    inp, O, L = _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0), (0, 63)], nrows=48)
+    """All 64 heads of the window + padding workload, element by element."""
+    inp, O, L = _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128")
     # every query sees at least itself or the keys before the padding: no -inf rows here
     assert np.all(np.isfinite(L))
 

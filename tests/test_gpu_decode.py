@@ -24,9 +24,18 @@ def run_decode(inp, nsplit):
     return o.t.cpu().numpy()
 
 
-def check(got, ref, what):
+def check(got, ref, what, dtype="bf16"):
+    """float32 inputs: normwise relative error <= 1e-5 per head (the float32 bar; o is a weighted mean and
+    crosses zero, so its elementwise relative error is unbounded).  bf16 inputs: <= 1e-2 absolute, and a
+    normwise 1e-4 as a diagnostic of the float32 statistics."""
     assert not np.isnan(got).any()
     err = np.abs(got - ref)
+    if dtype == "f32":
+        B, H = got.shape[:2]
+        for b in range(B):
+            for h in range(H):
+                assert_normwise(got[b, h], ref[b, h], 1e-5, what=f"{what} b={b} h={h}")
+        return
     assert err.max() <= 1e-2, f"{what}: max abs err {err.max():.3e}"
     assert_normwise(got, ref, 1e-4, what=what)
 
@@ -40,7 +49,7 @@ def test_decode_parity(dtype, B, H, Nkv, d, nsplit):
     print(f"decode {dtype} B={B} H={H} Nkv={Nkv} d={d} nsplit={nsplit}", flush=True)
     inp = decode_inputs(B, H, Nkv, d, seed=Nkv + nsplit, dtype=dtype)
     got = run_decode(inp, nsplit)
-    check(got, decode_ref(inp["q"], inp["k"], inp["v"]), f"decode {dtype}")
+    check(got, decode_ref(inp["q"], inp["k"], inp["v"]), f"decode {dtype}", dtype)
 
 
 def test_decode_split_invariance():

@@ -72,8 +72,7 @@ def test_softmax_rows_full_workload():
     x_np = softmax_rows_inputs(w["rows"], w["cols"], seed=w["seed"], sigma=w["sigma"])
     print("softmax_rows full 4096x4000", flush=True)
     y = _run_rows(x_np)
-    rows = np.random.default_rng(1).choice(w["rows"], 256, replace=False)
-    assert_f32_rel(y[rows], softmax_ref(x_np[rows]), what="full workload sample")
+    assert_f32_rel(y, softmax_ref(x_np), what="full workload, every row")
     assert np.max(np.abs(y.astype(np.float64).sum(axis=1) - 1.0)) <= w["cols"] * 2.0 ** -23
 
 
