@@ -152,6 +152,7 @@ def main():
     ti = torch.empty((tw["rows"], tw["k"]), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
+    print(f"bench: inputs ready in {t_setup:.1f} s", file=sys.stderr, flush=True)
 
     lib = osfa.load_library()
     stream = torch.cuda.current_stream()
@@ -232,7 +233,9 @@ def main():
     c3_tflops = c3_flops / (ms["attn_fwd_causal_2048"] * 1e-3) / 1e12
     c1_tflops = c1_flops / (ms["attn_fwd_f32_n1000"] * 1e-3) / 1e12
 
+    print(f"bench: {args.steps} timed steps done ({wall:.2f} s)", file=sys.stderr, flush=True)
     cpu = cpu_baseline(fin, fw, args.cpu_seconds)
+    print("bench: CPU oracle timed on the headline workload", file=sys.stderr, flush=True)
     cpu["per_config"] = cpu_baseline_per_config(args.cpu_seconds, c1in, c3in, sx, tx, dw)
 
     # Measured HBM bytes per launch (rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE,

@@ -205,6 +205,30 @@ attn_status_t attn_decode_splitkv(attn_dtype_t dtype, const void* q, const void*
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_decode_splitkv_noalloc -- attn_decode_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and the same
+ * result, with the split partials kept in a scratch array inside the
+ * library instead of a caller-supplied workspace.
+ *
+ * The scratch array is a device global of OSFA_DECODE_NOALLOC_SCRATCH_BYTES
+ * (4 MiB): each GPU the library runs on holds its own copy until the
+ * process ends.  The partials take B * H * nsplit * (d + 2) * 4 bytes
+ * (attn_decode_splitkv_workspace_bytes); larger requests return
+ * ATTN_ERR_INVALID_ARG.  The call allocates nothing (no hipMalloc, no
+ * hipFree); its first call on a device looks up that device's copy.
+ * Every call on one GPU shares that copy: calls whose kernels overlap on
+ * the same GPU (different streams, or another thread) race and give
+ * undefined results; calls ordered on one stream are safe.  The partials
+ * are fully rewritten by each call before they are read.
+ *
+ * Arguments, layout, scale and errors otherwise as attn_decode_splitkv.
+ */
+#define OSFA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+attn_status_t attn_decode_splitkv_noalloc(attn_dtype_t dtype, const void* q, const void* K, const void* V,
+                                          float* o, int B, int H, int Nkv, int d, int nsplit, hipStream_t stream);
+
+/*
  * online_softmax_rows -- y[r, :] = softmax(x[r, :]) for every row, float32.
  *
  * Pass 1 runs the online normalizer: a running pair (m, d), the sum d

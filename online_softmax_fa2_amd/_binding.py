@@ -51,6 +51,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_decode_splitkv_workspace_bytes.restype = sz
     lib.attn_decode_splitkv.argtypes = [i, p, p, p, p, i, i, i, i, i, p, sz, p]
     lib.attn_decode_splitkv.restype = i
+    lib.attn_decode_splitkv_noalloc.argtypes = [i, p, p, p, p, i, i, i, i, i, p]
+    lib.attn_decode_splitkv_noalloc.restype = i
     lib.online_softmax_rows.argtypes = [p, p, i, i, p]
     lib.online_softmax_rows.restype = i
     lib.online_softmax_topk_rows.argtypes = [p, p, p, p, i, i, i, p]
@@ -232,6 +234,27 @@ def attn_decode_splitkv(q, k, v, nsplit: int, out=None, workspace=None, stream=N
     _check(load_library().attn_decode_splitkv(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Nkv, d,
                                               int(nsplit), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                               _stream(stream)))
+    return out
+
+
+# Bytes of the partials attn_decode_splitkv_noalloc can hold (its scratch array).
+DECODE_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def attn_decode_splitkv_noalloc(q, k, v, nsplit: int, out, stream=None):
+    """attn_decode_splitkv with the partials in the library's scratch (no workspace); ``out`` must be supplied
+    ([B, H, d] float32), since the point of this entry is that nothing is allocated."""
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, Nkv, d = k.shape
+    if q.shape != (B, H, d) or v.shape != k.shape:
+        raise ValueError("q must be [B, H, d] and K, V [B, H, Nkv, d]")
+    if out is None:
+        raise ValueError("out must be supplied")
+    _need_out(out, (B, H, d), torch.float32, q, "out")
+    _need_device(q, k, v, out)
+    _check(load_library().attn_decode_splitkv_noalloc(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Nkv,
+                                                      d, int(nsplit), _stream(stream)))
     return out
 
 

@@ -191,6 +191,34 @@ attn_status_t attn_decode_splitkv(attn_dtype_t dtype, const void* q, const void*
   return hip_status(e, "attn_decode_splitkv", stream);
 }
 
+attn_status_t attn_decode_splitkv_noalloc(attn_dtype_t dtype, const void* q, const void* K, const void* V, float* o,
+                                          int B, int H, int Nkv, int d, int nsplit, hipStream_t stream) {
+  static_assert(osfa::kDecodeScratchBytes == OSFA_DECODE_NOALLOC_SCRATCH_BYTES, "header and library agree");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: unknown dtype %d", (int)dtype);
+  if (!q || !K || !V || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: null pointer");
+  if (B < 1 || H < 1 || Nkv < 1 || d < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: sizes must be >= 1 (B=%d H=%d Nkv=%d d=%d)", B, H,
+                Nkv, d);
+  if (d != 64 && d != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_splitkv_noalloc: d=%d not built (64 or 128)", d);
+  if (nsplit < 1 || nsplit > Nkv || nsplit > 4096)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: nsplit=%d must be in [1, min(Nkv, 4096)]", nsplit);
+  if ((long long)B * H * Nkv * d >= kMaxElems) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: too large");
+  if ((long long)B * H * nsplit >= (1LL << 31))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: grid too large");
+  const size_t need = attn_decode_splitkv_workspace_bytes(B, H, d, nsplit);
+  if (need > osfa::kDecodeScratchBytes)
+    return fail(ATTN_ERR_INVALID_ARG,
+                "attn_decode_splitkv_noalloc: partials need %zu bytes, more than the %zu-byte scratch (B*H*nsplit*(d+2)*4)",
+                need, osfa::kDecodeScratchBytes);
+  if (((uintptr_t)q | (uintptr_t)K | (uintptr_t)V) & 15)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: q, K, V must be 16-byte aligned");
+  if ((uintptr_t)o & 3) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_splitkv_noalloc: o must be 4-byte aligned");
+  osfa::DecodeArgs a{q, K, V, o, nullptr, B, H, Nkv, d, nsplit};
+  return hip_status(osfa::launch_decode_noalloc(a, dtype == ATTN_BF16, stream), "attn_decode_splitkv_noalloc", stream);
+}
+
 attn_status_t online_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream) {
   if (!x || !y) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: null pointer");
   if (rows < 1 || cols < 1) return fail(ATTN_ERR_INVALID_ARG, "online_softmax_rows: rows=%d cols=%d must be >= 1", rows, cols);

@@ -20,10 +20,20 @@
 //     same rule and written as the split's partial.
 // Partials (workspace, float32): [B, H, nsplit, D + 2] = (m, l, a[0..D)),
 // with m in log2 units of the scaled score (m = log2(e) * max score).
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace osfa {
+
+// Partials of attn_decode_splitkv_noalloc, the entry point for callers that
+// cannot allocate: a device global of kDecodeScratchBytes, one copy per GPU
+// the library runs on, held until the process ends.  Host code never uses
+// this name as an address; it uses the per-device pointer from
+// decode_scratch() below.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
 namespace {
 
 constexpr int kDecThreads = 256;
@@ -264,5 +274,37 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_decode<__bf16>(a, stream); }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) { return launch_decode<float>(a, stream); }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];  // device address of `scratch` per device, set on first use
+}  // namespace
+
+// The address of `scratch` on the current device, looked up once per device
+// with that device current (every GPU holds its own copy at its own address).
+hipError_t decode_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* raw = nullptr;
+    e = hipGetSymbolAddress(&raw, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (raw == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(raw);
+    g_scratch[dev].store(p, std::memory_order_release);  // racing first calls store the same address
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(const DecodeArgs& a_in, bool bf16, hipStream_t stream) {
+  DecodeArgs a = a_in;
+  const hipError_t e = decode_scratch(&a.ws);
+  if (e != hipSuccess) return e;
+  return bf16 ? launch_decode<__bf16>(a, stream) : launch_decode<float>(a, stream);
+}
 
 }  // namespace osfa

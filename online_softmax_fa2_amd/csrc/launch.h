@@ -56,6 +56,11 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+// The same kernels with the partials in the library's per-device scratch
+// array (a.ws is ignored); the caller has checked that they fit in
+// kDecodeScratchBytes.
+constexpr size_t kDecodeScratchBytes = size_t(4) << 20;
+hipError_t launch_decode_noalloc(const DecodeArgs& a, bool bf16, hipStream_t stream);
 
 hipError_t launch_softmax_rows(const float* x, float* y, int rows, int cols, hipStream_t stream);
 hipError_t launch_softmax_topk(const float* x, float* y, float* topv, int32_t* topi, int rows,

@@ -52,6 +52,7 @@ hipError_t launch_attn_fwd_fp8(const FwdArgs& a, float, float, hipStream_t) { ++
 hipError_t launch_attn_bwd_bf16(const BwdArgs&, hipStream_t) { ++g_launches; return g_result; }
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t) { ++g_launches; g_dec = a; return g_result; }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t) { ++g_launches; g_dec = a; return g_result; }
+hipError_t launch_decode_noalloc(const DecodeArgs& a, bool, hipStream_t) { ++g_launches; g_dec = a; return g_result; }
 hipError_t launch_softmax_rows(const float*, float*, int, int, hipStream_t) { ++g_launches; return g_result; }
 hipError_t launch_softmax_topk(const float*, float*, float*, int32_t*, int, int, int, hipStream_t) { ++g_launches; return g_result; }
 }  // namespace osfa
@@ -105,6 +106,16 @@ int main() {
   EXPECT(g_dec.Nkv == 131072 && g_dec.nsplit == 64 && g_dec.d == 128);
   EXPECT(attn_decode_splitkv(ATTN_BF16, P, P, P, F, 1, 32, 131072, 128, 64, P, ws - 4, nullptr) == ATTN_ERR_INVALID_ARG);
   EXPECT(attn_decode_splitkv(ATTN_F32, P, P, P, F, 1, 1, 10, 64, 11, P, ws, nullptr) == ATTN_ERR_INVALID_ARG);
+  // The allocation-free variant: same checks, and the partials must fit in its scratch.
+  g_launches = 0;
+  EXPECT(attn_decode_splitkv_noalloc(ATTN_BF16, P, P, P, F, 1, 32, 131072, 128, 64, nullptr) == ATTN_OK);
+  EXPECT(g_launches == 1 && g_dec.ws == nullptr && g_dec.nsplit == 64);
+  EXPECT(attn_decode_splitkv_noalloc(ATTN_BF16, P, P, P, F, 8, 32, 131072, 128, 64, nullptr) == ATTN_ERR_INVALID_ARG);
+  EXPECT(std::strstr(attn_last_error(), "scratch") != nullptr);
+  EXPECT(attn_decode_splitkv_noalloc(ATTN_BF16, P, P, P, F, 1, 32, 131072, 96, 64, nullptr) == ATTN_ERR_UNSUPPORTED);
+  EXPECT(attn_decode_splitkv_noalloc(ATTN_BF16, P + 8, P, P, F, 1, 32, 131072, 128, 64, nullptr) ==
+         ATTN_ERR_INVALID_ARG);
+  EXPECT(g_launches == 1);
 
   // Softmax and top-k (x == y allowed, partial overlap refused).
   EXPECT(online_softmax_rows(F, F, 4, 100, nullptr) == ATTN_OK);

@@ -292,6 +292,8 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
         "attn_fwd_fp8": lambda: _fp8(lib),
         "attn_bwd": lambda: _bwd(lib),
         "attn_decode_splitkv": lambda: _dec(lib),
+        "attn_decode_splitkv_noalloc": lambda: lib.attn_decode_splitkv_noalloc(bd.ATTN_BF16, FAKE, FAKE, FAKE, FAKE, 1,
+                                                                               2, 100, 128, 4, None),
         "online_softmax_rows": lambda: lib.online_softmax_rows(FAKE, FAKE, 4, 100, None),
         "online_softmax_topk_rows": lambda: lib.online_softmax_topk_rows(FAKE, None, FAKE * 2, FAKE * 3, 4, 100, 5,
                                                                          None),
