@@ -917,6 +917,33 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdParams p) {
 // O_w / sum 2^(m_w - M) l_w.
 // ---------------------------------------------------------------------------
 
+// The keys query i sees form one interval [lo, hi] (hi = lo - 1 when empty):
+// j < jmax, j <= i when causal, |i - j| < window when windowed -- the rule of
+// visible(), evaluated once per query instead of once per score.
+struct KeySpan {
+  int lo, hi;
+};
+__device__ __forceinline__ KeySpan key_span(const FwdParams& p, int jmax, int i) {
+  long long lo = 0, hi = (long long)jmax - 1;
+  if (p.causal) hi = min(hi, (long long)i);
+  if (p.window > 0) {
+    lo = max(lo, (long long)i - p.window + 1);
+    hi = min(hi, (long long)i + p.window - 1);
+  }
+  KeySpan k;
+  k.lo = (int)lo;
+  k.hi = (int)max(hi, lo - 1);
+  return k;
+}
+
+// Orders a wave's earlier LDS accesses before its later ones across lanes:
+// wavefront-scope release and acquire around the wave's own barrier.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int D, int S>
 __global__ __launch_bounds__(64 * S, 1) void fwd_f32_split_kernel(FwdParams p) {
   constexpr int BC = 32;        // keys per block
@@ -956,6 +983,7 @@ __global__ __launch_bounds__(64 * S, 1) void fwd_f32_split_kernel(FwdParams p) {
   }
 
   const KeyRange kr = key_range(p, b, q0);
+  const KeySpan span = key_span(p, kr.jmax, qi);
   const int kb_lo = kr.kbeg / BC;
   const int kb_hi = (kr.kend > kr.kbeg) ? (kr.kend + BC - 1) / BC : kb_lo;
   float* ks = lds + w * WREG;
@@ -972,14 +1000,16 @@ __global__ __launch_bounds__(64 * S, 1) void fwd_f32_split_kernel(FwdParams p) {
   for (int kb = kb_lo + w; kb < kb_hi; kb += S) {
     const int j0 = kb * BC;
     // This wave's block into its own region (rows past N read row N - 1;
-    // they are masked).  A wave's LDS accesses take effect in order, so the
-    // previous block's reads are done before these writes land.
+    // they are masked).  Other lanes read the previous block's rows from it,
+    // so the writes wait for those reads, and the reads below for the writes.
+    wave_sync();
     for (int idx = lane; idx < BC * D / 4; idx += 64) {
       const int row = idx / (D / 4), c4 = idx % (D / 4);
       const int j = min(j0 + row, N - 1);
       *reinterpret_cast<f32x4*>(ks + row * RS + 4 * c4) = *reinterpret_cast<const f32x4*>(Kg + (size_t)j * D + 4 * c4);
       *reinterpret_cast<f32x4*>(vs + row * RS + 4 * c4) = *reinterpret_cast<const f32x4*>(Vg + (size_t)j * D + 4 * c4);
     }
+    wave_sync();
     // S^T: lane l, register r holds key j0 + 8 (r/4) + 4 hf + r%4 of query qi.
     f32x16 s;
 #pragma unroll
@@ -987,15 +1017,15 @@ __global__ __launch_bounds__(64 * S, 1) void fwd_f32_split_kernel(FwdParams p) {
     const float* krow = ks + l32 * RS + (D / 2) * hf;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[kk], qreg[kk], s, 0, 0, 0);
-    bool interior = j0 + BC <= kr.jmax;
-    if (p.causal) interior = interior && j0 + BC - 1 <= q0;
-    if (p.window > 0) interior = interior && q0 + 31 - j0 < p.window && (p.causal || j0 + BC - 1 - q0 < p.window);
-    if (!interior) {
+    // Every block is masked, by selects: with a branch here (masked blocks
+    // only) the compiler read the last score register of the d = 128
+    // instance on the masked path 17 wait states after the MFMA that writes
+    // it, one fewer than the 18 it inserts in straight-line code, and wrote
+    // the stale value back.  Selects keep the reads in the MFMAs' own block.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (!visible(p, kr.jmax, qi, j)) s[r] = kNegInf;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      s[r] = (j < span.lo || j > span.hi) ? kNegInf : s[r];
     }
     float mx = kNegInf;
 #pragma unroll
@@ -1088,14 +1118,16 @@ hipError_t launch_attn_fwd_bf16_exp2_offload(const FwdArgs& a, int poly_every, h
 }
 
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream) {
-  // d = 64 with fewer 128-query tiles than CUs: 32-query workgroups whose 8
-  // waves split the keys.  (The d = 128 instance needs more than 256
-  // registers per lane; built that way it gave wrong rows on causal diagonal
-  // blocks, so d = 128 keeps the tile kernel.)
+  // Fewer 128-query tiles than CUs: 32-query workgroups whose waves split the
+  // keys (8 waves at d = 64; 4 at d = 128, whose per-wave K and V regions
+  // take 33 KB of LDS each).
   const long long tiles128 = (long long)a.B * a.H * ((a.N + kBr - 1) / kBr);
-  if (a.d == 64 && tiles128 < kSplitTilesBelow) {
+  if (tiles128 < kSplitTilesBelow) {
     const FwdParams p = make_params(a, 32);
-    hipLaunchKernelGGL((fwd_f32_split_kernel<64, 8>), dim3(grid_for(p)), dim3(512), 0, stream, p);
+    if (a.d == 128)
+      hipLaunchKernelGGL((fwd_f32_split_kernel<128, 4>), dim3(grid_for(p)), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_f32_split_kernel<64, 8>), dim3(grid_for(p)), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
   const FwdParams p = make_params(a, kBr);

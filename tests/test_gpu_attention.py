@@ -78,8 +78,10 @@ CASES = [
     (1, 2, 700, 128, True, 100, [650], 3),
     (2, 1, 500, 128, False, 60, [430, 500], 0),
     (2, 1, 333, 64, True, 0, [0, 200], 0),        # batch 0: every row fully masked
+    (2, 1, 333, 128, True, 0, [0, 200], 0),
     (1, 1, 400, 128, True, 1, None, 0),           # each row sees only itself
     (1, 1, 256, 64, True, 64, [100], 0),          # window + padding: rows 163.. see nothing
+    (1, 1, 256, 128, True, 64, [100], 0),
     (1, 3, 513, 128, False, 0, [257], 4),
     (3, 2, 127, 128, False, 1000, None, 0),
     (1, 1, 200, 64, False, 2**31 - 1, None, 0),   # window beyond N: no mask
@@ -183,8 +185,8 @@ def test_fwd_exp2_offload_full_window_pad_8192():
     (1, 32, 1030, 128, False, 0, None),
 ])
 def test_fwd_f32_tile_path(B, H, N, d, causal, window, kv_len):
-    """float32 launches with at least 256 tiles of 128 queries (and every d = 128 one) take the 128-query tile
-    kernel; d = 64 launches with fewer take the key-split kernel, which the other d = 64 cases here run."""
+    """float32 launches with at least 256 tiles of 128 queries take the 128-query tile kernel; launches with
+    fewer take the key-split kernel, which the other float32 cases here run (d = 64 and d = 128)."""
     assert B * H * ((N + 127) // 128) >= 256
     print(f"attn_fwd f32 tile path B={B} H={H} N={N} d={d}", flush=True)
     inp = attn_inputs(B, H, N, d, dtype="f32", seed=N + d, causal=causal, window=window, kv_len=kv_len)
