@@ -30,6 +30,11 @@
 // hold, per lane, 8 consecutive queries per 8 registers, which makes the
 // bf16 P and dS the B operands of dV^T += dO^T P and dK^T += Q^T dS (dO and
 // Q read transposed).
+//
+// Two waves per SIMD do not overlap one wave's VALU work with the other's
+// MFMAs, and an MFMA whose LDS operand was read just before it waits out the
+// read's latency; both kernels therefore keep a queue of operand fragments
+// in flight a few MFMAs ahead of their use.
 #include "device_common.h"
 #include "launch.h"
 #include "masks.h"
@@ -45,6 +50,10 @@ constexpr int kTile = 32 * kW;        // queries (dq) or keys (dkdv) per workgro
 constexpr int kQb = 32;               // queries per block in bwd_dkdv_kernel
 constexpr int NKK = D / 16;
 constexpr int NMD = D / 32;
+// LDS operand fragments in flight ahead of their MFMA: bwd_dq_kernel's A
+// operands, bwd_dkdv_kernel's A operands and its V rows.  Deeper queues do
+// not fit in the 256 registers of two waves per SIMD (they spill).
+constexpr int kDqAhead = 4, kKvAhead = 3, kVAhead = 2;
 
 struct BwdParams {
   const __bf16* q;
@@ -157,6 +166,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* blk, const TrOff& t, int m
 // dQ: query tiles of 128, key blocks of 64.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int RQ = kDqAhead;
   constexpr int BLK = kBc * D * 2;  // 16 KB
   constexpr int LOADS = 16;         // load instructions per block (1 KB each)
   __shared__ __attribute__((aligned(1024))) char k0[BLK];
@@ -242,14 +252,26 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   auto block = [&](int j, const char* kl, const char* vl) {
     const int j0 = (kb_lo + j) * kBc;
     if (!any_visible(p, jmax, qa, qb, j0, j0 + kBc - 1)) return;
+    // The block's 48 A operands in MFMA order: K rows (S^T), V rows (dP^T),
+    // K transposed (dQ^T).  RQ of them are in flight ahead of their MFMA.
+    auto frag = [&](int i) -> bf16x8 {
+      if (i < 16) return row_frag(kl, 32 * (i >> 3) + krow, i & 7, hf);
+      if (i < 32) return row_frag(vl, 32 * ((i - 16) >> 3) + krow, i & 7, hf);
+      return tr_frag(kl, tro, (i - 32) >> 2, i & 3);
+    };
+    bf16x8 fq[RQ];
+#pragma unroll
+    for (int i = 0; i < RQ; ++i) fq[i] = frag(i);
     f32x16 s[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(kl, 32 * kt + krow, kk, hf), qreg[kk], s[kt], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      s[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[i % RQ], qreg[i & 7], s[i >> 3], 0, 0, 0);
+      fq[i % RQ] = frag(i + RQ);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Register r of group kt holds key j0 + 32 kt + 16 (r / 8) + 8 hf + r % 8
     // of query qi: masked scores take P = 0, and so dS = 0.  P replaces S in
@@ -266,8 +288,12 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) dp[r] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(vl, 32 * kt + krow, kk, hf), doreg[kk], dp, 0, 0, 0);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int i = 16 + 8 * kt + kk;
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[i % RQ], doreg[kk], dp, 0, 0, 0);
+        fq[i % RQ] = frag(i + RQ);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         f32x8 f;
@@ -278,10 +304,12 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
     }
     // dQ^T += K^T dS^T: K read transposed, 16 keys per MFMA.
 #pragma unroll
-    for (int md = 0; md < NMD; ++md)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(kl, tro, md, g), ds[g >> 1][g & 1], acc[md], 0, 0, 0);
+    for (int i = 32; i < 48; ++i) {
+      const int md = (i - 32) >> 2, g = i & 3;
+      acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[i % RQ], ds[g >> 1][g & 1], acc[md], 0, 0, 0);
+      if (i + RQ < 48) fq[i % RQ] = frag(i + RQ);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   auto iter = [&](int j, const char* kl, const char* vl, char* kn, char* vn) {
@@ -318,10 +346,11 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
 // dK and dV: key tiles of 128, query blocks of 32.  Both 32 keys x 128
 // columns accumulators of a wave (128 VGPRs) and its K rows (32) are held in
 // registers; the V rows, needed only as the dP operand, are read from LDS
-// (staged once) and operand fragments are read just before their MFMA, which
-// keeps the kernel at two waves per SIMD.
+// (staged once).  Operand fragments are read a few MFMAs ahead, from offsets
+// formed next to the read, which keeps the kernel at two waves per SIMD.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int RA = kKvAhead, RV = kVAhead;
   constexpr int QBLK = kQb * D * 2;  // 8 KB
   __shared__ __attribute__((aligned(1024))) char q0b[QBLK];
   __shared__ __attribute__((aligned(1024))) char q1b[QBLK];
@@ -399,24 +428,57 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
       accv[md][r] = 0.0f;
     }
 
+  // Fragment offsets from four bases: under the XOR swizzle, chunk 2 kk + hf
+  // of a row is at kv_off(row, hf) ^ 32 kk, and the transposed read of
+  // column group md at its md = 0 offset ^ 64 md.
+  const int rbase = kv_off(qrow, hf), vbase = kv_off(32 * w + l32, hf);
+  const int tbase0 = tro.off[0][0], tbase1 = tro.off[1][0];
   auto block = [&](int j, const char* ql, const char* gl, const float* sl) {
     const int i0 = (qb_lo + j) * kQb;
     if (!any_visible(p, jmax, i0, i0 + kQb - 1, ja, jb)) return;
+    // The block's 32 A operands in MFMA order -- S and dP alternate over the
+    // 8 k-steps (Q rows, dO rows), then dO transposed (dV^T) and Q
+    // transposed (dK^T) -- with RA in flight, and the V rows (B operand of
+    // dP) with RV in flight.  The empty asm makes the bases new values each
+    // block, so the XORs stay beside their reads instead of 24 offsets
+    // living in registers across the loop.
+    int rb = rbase, vb = vbase, tb0 = tbase0, tb1 = tbase1;
+    asm volatile("" : "+v"(rb), "+v"(vb), "+v"(tb0), "+v"(tb1));
+    auto trf = [&](const char* blk, int md, int g) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(blk + (tb0 ^ (md << 6)) + 4096 * g));
+      const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(blk + (tb1 ^ (md << 6)) + 4096 * g));
+      const s16x8 hv = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      return __builtin_bit_cast(bf16x8, hv);
+    };
+    auto afrag = [&](int i) -> bf16x8 {
+      if (i < 16) return *reinterpret_cast<const bf16x8*>(((i & 1) ? gl : ql) + (rb ^ ((i >> 1) << 5)));
+      if (i < 24) return trf(gl, (i - 16) >> 1, i & 1);
+      return trf(ql, (i - 24) >> 1, i & 1);
+    };
+    auto vfrag = [&](int kk) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(vtile + (vb ^ (kk << 5))); };
+    bf16x8 fa[RA], fv[RV];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) fa[i] = afrag(i);
+#pragma unroll
+    for (int i = 0; i < RV; ++i) fv[i] = vfrag(i);
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s[r] = 0.0f;
       dp[r] = 0.0f;
     }
-    // Fragments are read one k-step ahead of their MFMAs (sched_barrier keeps
-    // the compiler from hoisting every read, which would not fit in VGPRs).
-    // (Fragments are read just before their MFMA: read-ahead registers are
-    // what the two accumulators need.)
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(ql, qrow, kk, hf), kreg[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(gl, qrow, kk, hf), row_frag(vtile, 32 * w + l32, kk, hf), dp,
-                                                   0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[(2 * kk) % RA], kreg[kk], s, 0, 0, 0);
+      fa[(2 * kk) % RA] = afrag(2 * kk + RA);
+      __builtin_amdgcn_sched_barrier(0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[(2 * kk + 1) % RA], fv[kk % RV], dp, 0, 0, 0);
+      fa[(2 * kk + 1) % RA] = afrag(2 * kk + 1 + RA);
+      if (kk + RV < NKK) fv[kk % RV] = vfrag(kk + RV);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Register r holds query i0 + 16 (r / 8) + 8 hf + r % 8 of key kj.
@@ -442,18 +504,15 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
       pb[t] = __builtin_convertvector(f, bf16x8);
       pv[t] = __builtin_convertvector(fp, bf16x8);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA (dO and Q read
-    // transposed).
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
 #pragma unroll
-    for (int i = 0; i < 2 * NMD; ++i) {
-      accv[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(gl, tro, i >> 1, i & 1), pv[i & 1], accv[i >> 1], 0,
-                                                             0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * NMD; ++i) {
-      acck[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ql, tro, i >> 1, i & 1), pb[i & 1], acck[i >> 1], 0,
-                                                             0, 0);
+    for (int i = 16; i < 32; ++i) {
+      const int md = (i & 7) >> 1;
+      if (i < 24)
+        accv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i % RA], pv[i & 1], accv[md], 0, 0, 0);
+      else
+        acck[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i % RA], pb[i & 1], acck[md], 0, 0, 0);
+      if (i + RA < 32) fa[i % RA] = afrag(i + RA);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
