@@ -243,13 +243,14 @@ def main():
     # of the kernel sources: reported only while the kernel is unchanged.
     from online_softmax_fa2_amd.rocprof_summary import lookup
     traffic_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
-    fwd_traffic = lookup("fwd_bf16_d128_kernel<4, 0>", traffic_file)
+    fwd_grid = acc.fwd_bf16_d128_grid(fw["B"], fw["H"], fw["N"])
+    fwd_traffic = lookup("fwd_bf16_d128_kernel<4, 0>", traffic_file, grid=fwd_grid)
     # Shader clock the forward kernel ran at (GRBM_GUI_ACTIVE per XCD over the
     # dispatch time, profiles/sq_counters.json): the matrix-core peak at that
     # clock is the nominal one scaled by clock / 2.4 GHz.
     sq_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sq_counters.json")
-    fwd_clock = lookup("fwd_bf16_d128_kernel<4, 0>", sq_file, "clock_ghz")
-    dec_traffic = lookup("decode_partial_kernel", traffic_file)
+    fwd_clock = lookup("fwd_bf16_d128_kernel<4, 0>", sq_file, "clock_ghz", grid=fwd_grid)
+    dec_traffic = lookup("decode_partial_kernel<bf16, 128>", traffic_file)
 
     out = {
         "metric": "attn fwd TFLOP/s & %MFMA peak (N=8K,d=128 bf16); split-KV decode HBM GB/s",

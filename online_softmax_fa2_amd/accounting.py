@@ -60,3 +60,10 @@ def softmax_bytes(rows: int, cols: int) -> int:
 def topk_bytes(rows: int, cols: int, k: int) -> int:
     """x read once, float32, plus the k values and indices written per row."""
     return rows * cols * 4 + rows * k * 8
+
+
+def fwd_bf16_d128_grid(B: int, H: int, N: int) -> int:
+    """Work-items of one bf16 d = 128 forward launch: a 256-thread workgroup per 128-query tile of every head,
+    the workgroup count rounded up to a multiple of the 8 XCDs.  Selects that launch's profile record."""
+    tiles = B * H * ((N + 127) // 128)
+    return (tiles + 7) // 8 * 8 * 256
