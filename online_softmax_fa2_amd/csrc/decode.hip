@@ -193,10 +193,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const T* __
 
 // One workgroup per (b, h): o = sum_c w_c a_c / sum_c w_c l_c with
 // w_c = 2^(m_c - M), M = max_c m_c, and w_c = 0 for an empty split.
-// Threads first read all (m_c, l_c) in parallel and reduce M and the
-// weighted l through LDS; then thread (d, g) sums the splits c = g mod G for
-// column d, and the G partial sums are combined through LDS.
+// Only the weights depend on M, so every thread issues its loads at once --
+// (m_c, l_c) of split c = tid and the first kMergeAhead values a_c[d] of its
+// column -- and the three steps (M, the weighted l, the weighted a) then
+// wait on one round of global latency instead of three.  Thread (d, g) sums
+// the splits c = g mod G for column d in increasing c, and the G partial
+// sums are combined through LDS; splits past the first pass (nsplit > 256,
+// or past kMergeAhead G) are read in the same order afterwards.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeAhead = 32;
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ ws,
                                                                      float* __restrict__ o, int nsplit) {
@@ -208,9 +213,20 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const float* part = ws + (size_t)bh * nsplit * (D + 2);
+  const int d = tid % D, g = tid / D;
 
-  float mloc = kNegInf;
-  for (int c = tid; c < nsplit; c += kMergeThreads) mloc = fmaxf(mloc, part[(size_t)c * (D + 2)]);
+  const bool own = tid < nsplit;
+  const float m0 = own ? part[(size_t)tid * (D + 2)] : kNegInf;
+  const float l0 = own ? part[(size_t)tid * (D + 2) + 1] : 0.0f;
+  float av[kMergeAhead];
+#pragma unroll
+  for (int i = 0; i < kMergeAhead; ++i) {
+    const int c = g + G * i;
+    av[i] = c < nsplit ? part[(size_t)c * (D + 2) + 2 + d] : 0.0f;
+  }
+
+  float mloc = m0;
+  for (int c = tid + kMergeThreads; c < nsplit; c += kMergeThreads) mloc = fmaxf(mloc, part[(size_t)c * (D + 2)]);
   mloc = wave_max(mloc);
   if (lane == 0) s_red[w] = mloc;
   __syncthreads();
@@ -220,7 +236,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
   __syncthreads();  // s_red is reused below
 
   float lloc = 0.0f;
-  for (int c = tid; c < nsplit; c += kMergeThreads) {
+  if (own) {
+    const float wgt = (m0 == kNegInf) ? 0.0f : fast_exp2(m0 - M);
+    s_w[tid] = wgt;
+    lloc = wgt * l0;
+  }
+  for (int c = tid + kMergeThreads; c < nsplit; c += kMergeThreads) {
     const float mc = part[(size_t)c * (D + 2)];
     const float wgt = (mc == kNegInf) ? 0.0f : fast_exp2(mc - M);
     s_w[c] = wgt;
@@ -233,9 +254,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
 #pragma unroll
   for (int i = 0; i < kMergeThreads / 64; ++i) lt += s_red[i];
 
-  const int d = tid % D, g = tid / D;
   float at = 0.0f;
-  for (int c = g; c < nsplit; c += G) at = fmaf(s_w[c], part[(size_t)c * (D + 2) + 2 + d], at);
+#pragma unroll
+  for (int i = 0; i < kMergeAhead; ++i) {
+    const int c = g + G * i;
+    if (c < nsplit) at = fmaf(s_w[c], av[i], at);
+  }
+  for (int c = g + G * kMergeAhead; c < nsplit; c += G) at = fmaf(s_w[c], part[(size_t)c * (D + 2) + 2 + d], at);
   s_acc[g][d] = at;
   __syncthreads();
   if (g == 0) {
