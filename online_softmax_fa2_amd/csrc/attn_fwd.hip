@@ -997,19 +997,39 @@ __global__ __launch_bounds__(64 * S, 1) void fwd_f32_split_kernel(FwdParams p) {
   float m_run = kNegInf, l_run = 0.0f;
   const float c = p.c;
 
+  // A block's K and V rows pass through registers on their way to LDS; the
+  // next block's are loaded while the current one is computed, so a wave
+  // waits on global memory once, before its first block.  Lane `lane` holds
+  // the 16-byte chunks lane + 64 t of the block (rows past N read row
+  // N - 1; they are masked).
+  constexpr int NLD = BC * D / 4 / 64;
+  f32x4 kbuf[NLD], vbuf[NLD];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int idx = lane + 64 * t;
+      const int row = idx / (D / 4), c4 = idx % (D / 4);
+      const int j = min(kb * BC + row, N - 1);
+      kbuf[t] = *reinterpret_cast<const f32x4*>(Kg + (size_t)j * D + 4 * c4);
+      vbuf[t] = *reinterpret_cast<const f32x4*>(Vg + (size_t)j * D + 4 * c4);
+    }
+  };
+  if (kb_lo + w < kb_hi) fetch(kb_lo + w);
   for (int kb = kb_lo + w; kb < kb_hi; kb += S) {
     const int j0 = kb * BC;
-    // This wave's block into its own region (rows past N read row N - 1;
-    // they are masked).  Other lanes read the previous block's rows from it,
-    // so the writes wait for those reads, and the reads below for the writes.
+    // This wave's block into its own region.  Other lanes read the previous
+    // block's rows from it, so the writes wait for those reads, and the
+    // reads below for the writes.
     wave_sync();
-    for (int idx = lane; idx < BC * D / 4; idx += 64) {
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int idx = lane + 64 * t;
       const int row = idx / (D / 4), c4 = idx % (D / 4);
-      const int j = min(j0 + row, N - 1);
-      *reinterpret_cast<f32x4*>(ks + row * RS + 4 * c4) = *reinterpret_cast<const f32x4*>(Kg + (size_t)j * D + 4 * c4);
-      *reinterpret_cast<f32x4*>(vs + row * RS + 4 * c4) = *reinterpret_cast<const f32x4*>(Vg + (size_t)j * D + 4 * c4);
+      *reinterpret_cast<f32x4*>(ks + row * RS + 4 * c4) = kbuf[t];
+      *reinterpret_cast<f32x4*>(vs + row * RS + 4 * c4) = vbuf[t];
     }
     wave_sync();
+    if (kb + S < kb_hi) fetch(kb + S);
     // S^T: lane l, register r holds key j0 + 8 (r/4) + 4 hf + r%4 of query qi.
     f32x16 s;
 #pragma unroll
