@@ -98,7 +98,10 @@ def main():
     # backward of the same workload
     bdo = up_bf16(grad_inputs(fw["B"], fw["H"], fw["N"], fw["d"], seed=fw["seed"])[0])
     bdq, bdk, bdv = torch.empty_like(fq), torch.empty_like(fq), torch.empty_like(fq)
-    bws = torch.empty(osfa.bwd_workspace_bytes(fw["B"], fw["H"], fw["N"]) // 4, dtype=torch.float32, device=dev)
+    # Room to store dS: the backward forms dQ from it instead of recomputing S and dP.
+    bws_bytes = max(osfa.bwd_workspace_bytes(fw["B"], fw["H"], fw["N"]),
+                    osfa.bwd_stored_ds_workspace_bytes(fw["B"], fw["H"], fw["N"], fw["causal"], fw["window"]))
+    bws = torch.empty((bws_bytes + 3) // 4, dtype=torch.float32, device=dev)
     bw_flops = acc.attn_bwd_flops(fw["B"], fw["H"], fw["N"], fw["d"], fw["causal"], fw["window"], fin.kv_len)
     # FP8 forward of the same workload
     f8 = attn_fp8_inputs(fw["B"], fw["H"], fw["N"], fw["d"], seed=fw["seed"], causal=fw["causal"],

@@ -147,6 +147,20 @@ attn_status_t attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O,
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
 
 /*
+ * attn_bwd_stored_ds_workspace_bytes -- bytes of workspace with which
+ * attn_bwd also stores dS (bf16, in tiles of 32 keys x 32 queries over the
+ * key blocks the mask lets each query block see) and forms dQ = scale dS K
+ * from the stored tiles instead of recomputing S and dP: attn_bwd_workspace_
+ * bytes(B, H, N) rounded up to 256, plus B * H * ceil(N / 32) * S * 2048,
+ * where S is the number of 32-key blocks one 32-query block can see (all of
+ * them without a window; about window / 32 + 1 causal, window / 16 + 2
+ * otherwise; `window` as attn_bwd takes it).  Returns 0 for invalid sizes
+ * and where one head's tiles would exceed 2^31 bytes (attn_bwd then always
+ * recomputes).
+ */
+size_t attn_bwd_stored_ds_workspace_bytes(int B, int H, int N, int causal, int window);
+
+/*
  * attn_bwd -- backward pass of attn_fwd: the gradients dQ, dK, dV of the
  * forward output O for an incoming gradient dO.
  *
@@ -165,7 +179,11 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N);
  * is [B, H, N] float32 as written by attn_fwd for the same Q, K, V.  dQ, dK,
  * dV are fully overwritten (rounded to nearest even).  workspace:
  * caller-owned device memory of at least attn_bwd_workspace_bytes(B, H, N)
- * bytes, 4-byte aligned; its contents on return are unspecified.
+ * bytes, 4-byte aligned; its contents on return are unspecified.  With at
+ * least attn_bwd_stored_ds_workspace_bytes(B, H, N, causal, window) bytes
+ * (and that function non-zero), dS is stored in the workspace once and dQ
+ * is a product with it; with less, dQ recomputes S and dP.  The two ways
+ * compute dS identically.
  * Supported: dtype ATTN_BF16 and d = 128 (others -> ATTN_ERR_UNSUPPORTED);
  * B, H, N >= 1; B * H * N * d < 2^40; N * d < 2^30.
  */

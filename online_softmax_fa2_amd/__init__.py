@@ -8,8 +8,9 @@ does not load the library; the first call does, and raises if it is not
 built.
 """
 from ._binding import (OsfaError, attn_bwd, attn_decode_splitkv, attn_decode_splitkv_noalloc, attn_fwd, attn_fwd_exp2_offload, attn_fwd_fp8,  # noqa: F401
-                       bwd_workspace_bytes, decode_workspace_bytes, load_library, online_softmax_rows,
-                       online_softmax_topk_rows)
+                       bwd_stored_ds_workspace_bytes, bwd_workspace_bytes, decode_workspace_bytes, load_library,
+                       online_softmax_rows, online_softmax_topk_rows)
 
-__all__ = ["attn_fwd", "attn_fwd_exp2_offload", "attn_fwd_fp8", "attn_bwd", "bwd_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_noalloc", "decode_workspace_bytes",
+__all__ = ["attn_fwd", "attn_fwd_exp2_offload", "attn_fwd_fp8", "attn_bwd", "bwd_workspace_bytes",
+           "bwd_stored_ds_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_noalloc", "decode_workspace_bytes",
            "online_softmax_rows", "online_softmax_topk_rows", "load_library", "OsfaError"]

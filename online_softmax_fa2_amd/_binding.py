@@ -45,6 +45,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd_stored_ds_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd_stored_ds_workspace_bytes.restype = sz
     lib.attn_bwd.argtypes = [i, p, p, p, p, p, p, p, p, p, i, i, i, i, f, i, i, p, p, sz, p]
     lib.attn_bwd.restype = i
     lib.attn_decode_splitkv_workspace_bytes.argtypes = [i, i, i, i]
@@ -178,9 +180,18 @@ def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(load_library().attn_bwd_workspace_bytes(B, H, N))
 
 
+def bwd_stored_ds_workspace_bytes(B: int, H: int, N: int, causal: bool = False, window: int = 0) -> int:
+    """Workspace bytes with which attn_bwd stores dS and forms dQ from it (0: that way does not apply)."""
+    return int(load_library().attn_bwd_stored_ds_workspace_bytes(B, H, N, int(bool(causal)), int(window)))
+
+
 def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False, window: int = 0,
-             kv_len=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """(dQ, dK, dV) of attention for [B, H, N, d] bf16 tensors, given O and LSE from attn_fwd."""
+             kv_len=None, dq=None, dk=None, dv=None, workspace=None, stream=None, stored_ds: bool = True):
+    """(dQ, dK, dV) of attention for [B, H, N, d] bf16 tensors, given O and LSE from attn_fwd.
+
+    Without a `workspace`, one is allocated: large enough to store dS (the faster way) when `stored_ds` and
+    that way applies, else the minimum (dQ recomputes S and dP).  A given workspace decides by its size.
+    """
     if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, o, dout)):
         raise ValueError("q, k, v, o, dout must share one dtype")
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
@@ -201,8 +212,10 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = F
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     need = bwd_workspace_bytes(B, H, N)
+    if stored_ds:
+        need = max(need, bwd_stored_ds_workspace_bytes(B, H, N, causal, window))
     if workspace is None:
-        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
     _need_device(q, k, v, o, dout, lse, kv_len, dq, dk, dv, workspace)
     _check(load_library().attn_bwd(_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),

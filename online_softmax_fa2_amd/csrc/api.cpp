@@ -131,6 +131,19 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N) {
   return 2 * (size_t)B * H * N * sizeof(float);
 }
 
+// The dS tiles start at the D / LSE part rounded up to 256 bytes.
+static size_t bwd_ds_offset(int B, int H, int N) { return (attn_bwd_workspace_bytes(B, H, N) + 255) / 256 * 256; }
+
+size_t attn_bwd_stored_ds_workspace_bytes(int B, int H, int N, int causal, int window) {
+  if (B < 1 || H < 1 || N < 1 || window < 0 || (causal != 0 && causal != 1)) return 0;
+  const int w = window > N ? N : window;  // as the launcher clamps it
+  const long long head = osfa::ds_head_bytes(N, causal, w);
+  if (head >= (1LL << 31)) return 0;
+  const double total = (double)B * H * (double)head;
+  if (total > 9.0e18) return 0;
+  return bwd_ds_offset(B, H, N) + (size_t)B * H * (size_t)head;
+}
+
 attn_status_t attn_bwd(attn_dtype_t dtype, const void* Q, const void* K, const void* V, const void* O, const void* dO,
                        const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d, float scale,
                        int causal, int window, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
@@ -157,7 +170,11 @@ attn_status_t attn_bwd(attn_dtype_t dtype, const void* Q, const void* K, const v
     return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned");
   if (((uintptr_t)LSE | (uintptr_t)workspace | (uintptr_t)kv_len) & 3)
     return fail(ATTN_ERR_INVALID_ARG, "attn_bwd: LSE, workspace and kv_len must be 4-byte aligned");
-  osfa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, kv_len, static_cast<float*>(workspace), B, H, N, d, scale, causal, window};
+  // Room for the dS tiles: store dS once and form dQ from it.
+  const size_t stored = attn_bwd_stored_ds_workspace_bytes(B, H, N, causal, window);
+  void* ds = (stored != 0 && workspace_bytes >= stored) ? static_cast<char*>(workspace) + bwd_ds_offset(B, H, N) : nullptr;
+  osfa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, kv_len, static_cast<float*>(workspace), ds, B, H, N, d, scale, causal,
+                  window};
   return hip_status(osfa::launch_attn_bwd_bf16(a, stream), "attn_bwd", stream);
 }
 

@@ -35,6 +35,8 @@
 // MFMAs, and an MFMA whose LDS operand was read just before it waits out the
 // read's latency; both kernels therefore keep a queue of operand fragments
 // in flight a few MFMAs ahead of their use.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "masks.h"
@@ -74,6 +76,9 @@ struct BwdParams {
   int causal, window;
   int n_tiles;  // ceil(N / kTile)
   int total;    // B * H * n_tiles
+  __bf16* ds;   // stored-dS tiles (launch.h: ds_span, ds_first), or nullptr
+  int nqb;      // ceil(N / 32): query blocks per head
+  int span;     // tile slots per query block
 };
 
 // Workgroups go to the 8 XCDs round-robin; each XCD takes a contiguous range
@@ -82,14 +87,14 @@ struct Tile {
   int bh, t0;
   bool valid;
 };
-__device__ __forceinline__ Tile map_tile(const BwdParams& p, bool ascending) {
+__device__ __forceinline__ Tile map_tile(const BwdParams& p, bool ascending, int tile_rows = kTile) {
   const int per_xcd = gridDim.x / 8;  // grid padded to a multiple of 8
   const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   Tile t;
   t.valid = logical < p.total;
   t.bh = logical / p.n_tiles;
   const int r = logical - t.bh * p.n_tiles;
-  t.t0 = (ascending ? r : p.n_tiles - 1 - r) * kTile;
+  t.t0 = (ascending ? r : p.n_tiles - 1 - r) * tile_rows;
   return t;
 }
 
@@ -114,6 +119,14 @@ __device__ __forceinline__ bool any_visible(const BwdParams& p, int jmax, int qa
   }
   return true;
 }
+// any_visible without branches (a per-lane value for the stored-dS loads).
+__device__ __forceinline__ bool any_visible_sel(const BwdParams& p, int jmax, int qa, int qb, int ja, int jb) {
+  const bool w = p.window > 0;
+  const bool c = ja <= qb && (!w | (qa - jb < p.window));
+  const bool n = !w | ((qa - jb < p.window) & (ja - qb < p.window));
+  return (ja < jmax) & (p.causal ? c : n);
+}
+
 // Buffer loads straight to LDS of rows [r0, r0 + 4 NLD) of a [N, 128] bf16
 // matrix in the layout of tile_layout.h: load t of wave w fills 1 KB (rows
 // 4 (w + kW t) .. + 3 of the block).  Rows past N read row N - 1.
@@ -349,6 +362,7 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
 // (staged once).  Operand fragments are read a few MFMAs ahead, from offsets
 // formed next to the read, which keeps the kernel at two waves per SIMD.
 // ---------------------------------------------------------------------------
+template <bool kStoreDs>
 __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int RA = kKvAhead, RV = kVAhead;
   constexpr int QBLK = kQb * D * 2;  // 8 KB
@@ -386,6 +400,17 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * D), 0, N * D * 2, kBufDword3);
   const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse2 + head), 0, N * 4, kBufDword3);
   const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.delta + head), 0, N * 4, kBufDword3);
+  // Stored dS of this head (< 2^31 bytes, checked by the host).
+  const int ds_hbytes = kStoreDs ? p.nqb * p.span * (kDsTile * kDsTile * 2) : 0;
+  const __amdgpu_buffer_rsrc_t dsrs = __builtin_amdgcn_make_buffer_rsrc(
+      kStoreDs ? (void*)(p.ds + (size_t)tile.bh * p.nqb * p.span * (kDsTile * kDsTile)) : nullptr, 0, ds_hbytes,
+      kBufDword3);
+  auto store_ds = [&](int off, const bf16x8 (&v)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[t]), dsrs, off + (16 * t + 8 * hf) * 2, 0,
+                                             kCpolNT);
+  };
   auto load_block = [&](int j, char* qd, char* gd, float* sd) {
     const int r0 = (qb_lo + j) * kQb;
     stage_rows<8>(qrs, qd, r0, N, w, lane);
@@ -414,6 +439,9 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
     stage_rows<32>(vrs, vtile, k0, N, w, lane);
   }
   if (nblk > 0) load_block(0, q0b, g0b, st0);
+  bool pending = false;  // a block's dS waits in pend for its store
+  int pend_off = 0;
+  bf16x8 pend[2];
   const float c = p.c;
   const int ja = k0 + 32 * w, jb = ja + 31;
   const int qrow = perm_key(l32);
@@ -504,6 +532,15 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
       pb[t] = __builtin_convertvector(f, bf16x8);
       pv[t] = __builtin_convertvector(fp, bf16x8);
     }
+    // Stored-dS path: this block's dS (32 keys x 32 queries, key-major) for
+    // its tile slot; lane (key l32, half hf) holds queries 16 t + 8 hf .. + 7.
+    if constexpr (kStoreDs) {
+      const int qb = i0 / kDsTile;
+      pend_off = ((qb * p.span + ja / kDsTile - ds_first(qb, p.window)) * (kDsTile * kDsTile) + l32 * kDsTile) * 2;
+      pend[0] = pb[0];
+      pend[1] = pb[1];
+      pending = true;
+    }
     // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
 #pragma unroll
     for (int i = 16; i < 32; ++i) {
@@ -517,9 +554,17 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
+  // With stored dS a block's dS is stored at the start of the next
+  // iteration, after its wait and barrier: the wait for a block's loads
+  // (vmcnt counts stores too) then finds the stores a whole block old
+  // instead of just issued.
   auto iter = [&](int j, const char* ql, const char* gl, const float* sl, char* qn, char* gn, float* sn) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    if constexpr (kStoreDs) {
+      if (pending) store_ds(pend_off, pend);
+      pending = false;
+    }
     if (j + 1 < nblk) load_block(j + 1, qn, gn, sn);
     block(j, ql, gl, sl);
   };
@@ -530,6 +575,9 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
     iter(j + 1, q1b, g1b, st1, q0b, g0b, st0);
   }
   if (j < nblk) iter(j, q0b, g0b, st0, q1b, g1b, st1);
+  if constexpr (kStoreDs) {
+    if (pending) store_ds(pend_off, pend);
+  }
   // No load into LDS may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -547,6 +595,292 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
   if (kj < N) {
     store(p.dk + (head + kj) * D, acck, p.scale);
     store(p.dv + (head + kj) * D, accv, 1.0f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stored-dS path.  bwd_dkdv_kernel also writes each visible block's dS (the
+// tiles of launch.h), and dQ = scale dS K becomes a product over the stored
+// tiles instead of a second pass computing S and dP: 6d FLOPs per visible
+// pair fewer.  D and LSE log2(e), which bwd_dkdv_kernel needs first, come
+// from bwd_prep_kernel.
+// ---------------------------------------------------------------------------
+
+// D_i = sum_d dO_id O_id and LSE_i log2(e) (+inf for a row with no key): the
+// lanes, products and sums of bwd_dq_kernel's prologue, so both paths use the
+// same values.  The tile's O and dO rows come in by coalesced buffer loads to
+// LDS (the swizzled block layout), and each lane then reads its 16-byte
+// pieces from there in bwd_dq_kernel's order.
+__global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char ol[kTile * D * 2];  // 32 KB
+  __shared__ __attribute__((aligned(1024))) char gl[kTile * D * 2];
+  const Tile tile = map_tile(p, false);
+  if (!tile.valid) return;
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)tile.bh * N;
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)(p.o + head * D), 0, N * D * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * D), 0, N * D * 2, kBufDword3);
+  // Rows past N read row N - 1 (not stored below).
+  stage_rows<kTile / 4>(ors, ol, tile.t0, N, w, lane);
+  stage_rows<kTile / 4>(grs, gl, tile.t0, N, w, lane);
+  const int qi = tile.t0 + 32 * w + l32;
+  const bool qok = qi < N;
+  const float lse_in = qok ? p.lse[head + qi] : kNegInf;
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  float dlt = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const u32x4 a = __builtin_bit_cast(u32x4, row_frag(ol, 32 * w + l32, kk, hf));
+    const u32x4 g = __builtin_bit_cast(u32x4, row_frag(gl, 32 * w + l32, kk, hf));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dlt = fmaf(bf16_lo(a[e]), bf16_lo(g[e]), dlt);
+      dlt = fmaf(bf16_hi(a[e]), bf16_hi(g[e]), dlt);
+    }
+  }
+  dlt = sum_halves(dlt);
+  const float lse2 = lse_in == kNegInf ? __builtin_huge_valf() : lse_in * kLog2e;
+  if (qok && hf == 0) {
+    p.delta[head + qi] = dlt;
+    p.lse2[head + qi] = lse2;
+  }
+}
+
+// dQ^T += K^T dS^T over the stored tiles.  A workgroup of 4 waves (one per
+// CU, one wave per SIMD) owns 256 queries, 64 per wave, and walks its key
+// range in blocks of 64.  The operands come from LDS: K^T (transposed reads
+// of the K block, the same for every wave) and dS^T (transposed reads of the
+// wave's own queries).  What one wave reads per MFMA sets the LDS traffic,
+// and with 64 queries a wave reads each K^T fragment once for two MFMAs:
+// 24 KB of reads per wave for 32 MFMAs per block.  The stored dS is
+// streamed from HBM once, by non-temporal loads that leave K in L2.  Each
+// wave holds its 12 16-byte pieces of the next two blocks (K rows, then dS)
+// in a ring of registers; while it multiplies block j it writes block j + 1
+// from the ring to the other LDS stage (the swizzled block layout: K, then
+// dS for queries 0..127 and 128..255), one piece per MFMA pair, and reloads
+// each piece's registers with block j + 3.  A tile no query of its block
+// sees is loaded from past the end of the buffer and reads as zeros.  Every
+// accumulator takes its key groups in the order of bwd_dq_kernel.
+constexpr int kDqsWaves = 4;
+constexpr int kDqsQg = 2;                          // 32-query groups per wave
+constexpr int kDqsTile = 32 * kDqsQg * kDqsWaves;  // queries per workgroup
+constexpr int kDqsRing = 2;                        // ring slots (blocks) per wave
+__global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p) {
+  constexpr int BLK = kBc * D * 2;        // 16 KB
+  constexpr int KLOADS = 16 / kDqsWaves;  // 16-byte K pieces per lane per block
+  constexpr int SLOADS = 32 / kDqsWaves;  // 16-byte dS pieces per lane per block
+  constexpr int AHEAD = 4;                // K^T fragments in flight
+  static_assert(kDqsTile == 256, "two LDS halves of 128 queries");
+  // Two LDS stages of (K block, dS for queries 0..127, dS for 128..255).
+  __shared__ __attribute__((aligned(1024))) char k0[BLK], k1[BLK];
+  __shared__ __attribute__((aligned(1024))) char s0[2 * BLK], s1[2 * BLK];
+
+  const Tile tile = map_tile(p, false, kDqsTile);
+  if (!tile.valid) return;
+  const int b = tile.bh / p.H;
+  const int q0 = tile.t0;
+  const int N = p.N;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)tile.bh * N;
+  const int jmax = key_limit(p, b);
+
+  // Key range of the tile (as bwd_dq_kernel, for 256 queries).
+  int kend = jmax;
+  if (p.causal) kend = min(kend, q0 + kDqsTile);
+  if (p.window > 0 && !p.causal) kend = min(kend, q0 + kDqsTile - 1 + p.window);
+  const int kbeg = p.window > 0 ? max(0, q0 - p.window + 1) : 0;
+  const int kb_lo = kbeg / kBc;
+  const int nblk = kend > kbeg ? (kend + kBc - 1) / kBc - kb_lo : 0;
+
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + head * D), 0, N * D * 2, kBufDword3);
+  const int hbytes = p.nqb * p.span * (kDsTile * kDsTile * 2);  // < 2^31 (checked by the host)
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ds + (size_t)tile.bh * p.nqb * p.span * (kDsTile * kDsTile)), 0, hbytes, kBufDword3);
+
+  // Piece t of a block for this lane: K row 4 u + lane / 16 (u = w + 4 t),
+  // or dS unit u = w + 4 t (half u / 16, key rows 4 (u % 16) + lane / 16);
+  // LDS position lane % 16 of the row holds chunk (lane % 16) ^ swz(row).
+  // Per dS piece the query block and the key rows are fixed; a key block
+  // only moves the 32-key tile, so the offset is base + 2048 (tile index)
+  // and visibility is a range of the tile's first key.
+  int sbase[SLOADS], slo[SLOADS], shi[SLOADS];
+#pragma unroll
+  for (int t = 0; t < SLOADS; ++t) {
+    const int u = w + kDqsWaves * t;
+    const int row = 4 * (u & 15) + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    const int qb = q0 / kDsTile + 4 * (u >> 4) + (c >> 2);
+    const int qa = kDsTile * qb, qz = qa + kDsTile - 1;
+    // A 32-key tile starting at ja is seen by some query of [qa, qz] iff
+    // ja < jmax, causal: ja <= qz, window: qa - (ja + 31) < W and
+    // (non-causal) ja - qz < W.
+    int hi = jmax - 1;
+    if (p.causal) hi = min(hi, qz);
+    else if (p.window > 0) hi = min(hi, qz + p.window - 1);
+    if (qb >= p.nqb) hi = -1;
+    shi[t] = hi;
+    slo[t] = p.window > 0 ? qa - kDsTile + 2 - p.window : 0;
+    sbase[t] = ((qb * p.span - ds_first(qb, p.window)) * (kDsTile * kDsTile) + (row % kDsTile) * kDsTile + 8 * (c & 3)) * 2 +
+               (row / kDsTile) * (kDsTile * kDsTile * 2);
+  }
+  u32x4 kr[kDqsRing][KLOADS], sr[kDqsRing][SLOADS];
+  auto load_k = [&](int j, int t) {
+    const int row = 4 * (w + kDqsWaves * t) + (lane >> 4);
+    const int grow = min((kb_lo + j) * kBc + row, N - 1);
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(krs, (grow * D + 8 * ((lane & 15) ^ swz(row))) * 2, 0, 0));
+  };
+  auto load_s = [&](int j, int t) {
+    const int j0 = (kb_lo + j) * kBc;
+    const int ja = j0 + ((4 * ((w + kDqsWaves * t) & 15) + (lane >> 4)) & kDsTile);  // first key of the lane's tile
+    const bool vis = (ja >= slo[t]) & (ja <= shi[t]);
+    const unsigned off = vis ? (unsigned)sbase[t] + (unsigned)j0 * (kDsTile * 2) : (unsigned)hbytes;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, (int)off, 0, kCpolNT));
+  };
+  auto fetch = [&](int j, u32x4 (&kd)[KLOADS], u32x4 (&sd)[SLOADS]) {
+#pragma unroll
+    for (int t = 0; t < KLOADS; ++t) kd[t] = load_k(j, t);
+#pragma unroll
+    for (int t = 0; t < SLOADS; ++t) sd[t] = load_s(j, t);
+  };
+  // Piece pc (K pieces first, then dS) of the block in ring slot `slot`:
+  // written to LDS stage (kl, sl), then the slot's piece is reloaded with
+  // block jn.
+  auto move = [&](int pc, u32x4 (&kd)[KLOADS], u32x4 (&sd)[SLOADS], char* kl, char* sl, int jn) __attribute__((always_inline)) {
+    if (pc < KLOADS) {
+      *reinterpret_cast<u32x4*>(kl + (w + kDqsWaves * pc) * 1024 + lane * 16) = kd[pc];
+      kd[pc] = load_k(jn, pc);
+    } else {
+      const int t = pc - KLOADS;
+      *reinterpret_cast<u32x4*>(sl + (w + kDqsWaves * t) * 1024 + lane * 16) = sd[t];
+      sd[t] = load_s(jn, t);
+    }
+  };
+
+  const int qa = q0 + 32 * kDqsQg * w, qz = qa + 32 * kDqsQg - 1;
+  const TrOff tro = tr_offsets(lane);
+  // dS^T read offsets of query group qg of the wave: queries 64 w + 32 qg of
+  // the tile are column group 2 (w % 2) + qg of half w / 2.
+  int soff[kDqsQg][2];
+  {
+    const int tr_g = lane >> 4, tr_j = lane & 15;
+    const int rowoff = 8 * (tr_g >> 1) + (tr_j >> 2);
+    const int col = 16 * (tr_g & 1) + 4 * (tr_j & 3);
+#pragma unroll
+    for (int qg = 0; qg < kDqsQg; ++qg)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        soff[qg][r] = (w >> 1) * BLK + kv_off(4 * r + rowoff, (32 * (2 * (w & 1) + qg) + col) >> 3) + (tr_j & 1) * 8;
+  }
+  auto sfrag = [&](const char* blk, int qg, int g) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x4 h[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(blk + soff[qg][r] + 4096 * g));
+    const s16x8 hv = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8, hv);
+  };
+  f32x16 acc[kDqsQg][NMD];
+#pragma unroll
+  for (int qg = 0; qg < kDqsQg; ++qg)
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[qg][md][r] = 0.0f;
+
+  // The MFMAs of block j (stage kl, sl) with the 12 pieces of the next
+  // block moved to the other stage between them, one per MFMA pair.  A wave
+  // that sees none of block j skips the reads and MFMAs but moves the same
+  // pieces in the same order: one path for the loads, so that the compiler
+  // keeps the ring in the same registers.
+  constexpr int NPC = KLOADS + SLOADS;
+  static_assert(NPC <= 16, "one piece per MFMA pair");
+  auto block = [&](int j, const char* kl, const char* sl, u32x4 (&kd)[KLOADS], u32x4 (&sd)[SLOADS], char* kn, char* sn,
+                   int jn) __attribute__((always_inline)) {
+    const int j0 = (kb_lo + j) * kBc;
+    const bool vis = any_visible(p, jmax, qa, qz, j0, j0 + kBc - 1);
+    bf16x8 bs[kDqsQg][4];
+    bf16x8 fk[AHEAD];
+    if (vis) {
+#pragma unroll
+      for (int qg = 0; qg < kDqsQg; ++qg) bs[qg][0] = sfrag(sl, qg, 0);
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) fk[i] = tr_frag(kl, tro, i & 3, i >> 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int g = i >> 2, md = i & 3;
+      if (vis) {
+        if (md == 0 && g < 3) {  // dS^T of the next key group, four steps ahead
+#pragma unroll
+          for (int qg = 0; qg < kDqsQg; ++qg) bs[qg][g + 1] = sfrag(sl, qg, g + 1);
+        }
+#pragma unroll
+        for (int qg = 0; qg < kDqsQg; ++qg)
+          acc[qg][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[i % AHEAD], bs[qg][g], acc[qg][md], 0, 0, 0);
+        if (i + AHEAD < 16) fk[i % AHEAD] = tr_frag(kl, tro, (i + AHEAD) & 3, (i + AHEAD) >> 2);
+      }
+      if (i < NPC) move(i, kd, sd, kn, sn, jn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // One workgroup barrier per block: before it, every wave's LDS writes of
+  // the next block are done (lgkmcnt(0)) and its reads of the current one
+  // were consumed by MFMAs.  It is a bare s_barrier between wavefront-scope
+  // fences: __syncthreads' workgroup fence would also wait for every load in
+  // flight in the register ring.
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt left at their maxima
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // Block b sits in ring slot b % 2.  Iteration j multiplies block j (stage
+  // j % 2) and moves block j + 1 from slot (j + 1) % 2 to stage (j + 1) % 2,
+  // refilling the slot with block j + 3.  The loop runs an even number of
+  // iterations; one past nblk moves and reads blocks no query sees.
+  static_assert(kDqsRing == 2, "block j + 1 sits in slot (j + 1) % 2");
+  auto iter = [&](int j, auto step_c) {
+    constexpr bool odd = decltype(step_c)::value;  // j % 2
+    constexpr int SN = odd ? 0 : 1;                // slot of block j + 1
+    block(j, odd ? k1 : k0, odd ? s1 : s0, kr[SN], sr[SN], odd ? k0 : k1, odd ? s0 : s1, j + kDqsRing + 1);
+    barrier();
+  };
+  if (nblk > 0) {
+#pragma unroll
+    for (int i = 0; i < kDqsRing; ++i) fetch(i, kr[i], sr[i]);
+#pragma unroll
+    for (int pc = 0; pc < NPC; ++pc) move(pc, kr[0], sr[0], k0, s0, kDqsRing);
+    barrier();
+    for (int j = 0; j < nblk; j += 2) {
+      iter(j, std::integral_constant<int, 0>());
+      iter(j + 1, std::integral_constant<int, 1>());
+    }
+  }
+
+#pragma unroll
+  for (int qg = 0; qg < kDqsQg; ++qg) {
+    const int qi = qa + 32 * qg + l32;
+    if (qi < N) {
+      __bf16* dst = p.dq + (head + qi) * D;
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          u32x2 wv;
+          wv[0] = pack_bf16x2(acc[qg][md][4 * rq + 0] * p.scale, acc[qg][md][4 * rq + 1] * p.scale);
+          wv[1] = pack_bf16x2(acc[qg][md][4 * rq + 2] * p.scale, acc[qg][md][4 * rq + 3] * p.scale);
+          *reinterpret_cast<u32x2*>(dst + 32 * md + 8 * rq + 4 * hf) = wv;
+        }
+    }
   }
 }
 
@@ -578,12 +912,29 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   p.window = a.window > a.N ? a.N : a.window;
   p.n_tiles = (a.N + kTile - 1) / kTile;
   p.total = a.B * a.H * p.n_tiles;
+  p.ds = static_cast<__bf16*>(a.ds);
+  p.nqb = (a.N + kDsTile - 1) / kDsTile;
+  p.span = (int)ds_span(a.N, a.causal, p.window);
   const unsigned grid = (unsigned)((p.total + 7) / 8 * 8);
+  if (p.ds) {
+    // D and LSE log2(e); dK, dV and the dS tiles; dQ from the tiles.
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid), dim3(kT), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(grid), dim3(kT), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    BwdParams pq = p;  // 256-query tiles
+    pq.n_tiles = (a.N + kDqsTile - 1) / kDqsTile;
+    pq.total = a.B * a.H * pq.n_tiles;
+    hipLaunchKernelGGL(bwd_dqs_kernel, dim3((unsigned)((pq.total + 7) / 8 * 8)), dim3(64 * kDqsWaves), 0, stream, pq);
+    return hipGetLastError();
+  }
   // dQ first: it also writes D and LSE log2(e), which bwd_dkdv_kernel reads.
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kT), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid), dim3(kT), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(grid), dim3(kT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -40,11 +40,35 @@ struct BwdArgs {
   void* dv;
   const int32_t* kv_len;  // device [B] or nullptr
   float* ws;              // [2, B, H, N]: D and LSE in log2 units
+  void* ds;               // stored-dS tiles (bf16), or nullptr: dQ recomputes S and dP
   int B, H, N, d;
   float scale;
   int causal, window;
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
+// Stored dS of the backward: bf16 tiles of 32 keys x 32 queries (key-major,
+// 2 KB), per head ceil(N / 32) query blocks of ds_span() tile slots; the tile
+// of query block qb and key block kb sits in slot kb - ds_first(qb).  Every
+// key block some query of block qb can see lies in that range.  `window` is
+// the window after clamping to N (0 = none).
+constexpr int kDsTile = 32;
+constexpr long long ds_span(int N, int causal, int window) {
+  const long long nb = (N + kDsTile - 1) / kDsTile;
+  if (window <= 0) return nb;
+  // causal: key blocks from that of 32 qb - W + 1 to qb; otherwise also up
+  // to that of 32 qb + 31 + W - 1.
+  const long long span = causal ? 1 + (window - 1 + kDsTile - 1) / kDsTile : (2LL * window + 29) / kDsTile + 2;
+  return span < nb ? span : nb;
+}
+constexpr int ds_first(int qb, int window) {
+  const int lo = kDsTile * qb - window + 1;
+  return (window > 0 && lo > 0) ? lo / kDsTile : 0;
+}
+// Bytes of one head's tiles (the kernels address them with 32-bit offsets).
+constexpr long long ds_head_bytes(int N, int causal, int window) {
+  return (long long)((N + kDsTile - 1) / kDsTile) * ds_span(N, causal, window) * kDsTile * kDsTile * 2;
+}
 
 struct DecodeArgs {
   const void* q;

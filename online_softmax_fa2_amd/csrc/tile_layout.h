@@ -22,6 +22,9 @@ constexpr int kBc = 64;  // rows (keys or queries) per staged block
 constexpr int kWaitVmcnt0 = 0x0F70;
 // Word 3 of a raw buffer resource (gfx9 family: 32-bit data format).
 constexpr int kBufDword3 = 0x00020000;
+// Cache-policy operand of a buffer load: the non-temporal bit (gfx94x/gfx950
+// encoding), for data read once that should not displace reused lines.
+constexpr int kCpolNT = 2;
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int kv_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }

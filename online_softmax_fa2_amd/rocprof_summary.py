@@ -42,6 +42,9 @@ KERNEL_SOURCES = {
     "softmax_topk_kernel": ["csrc/softmax.hip", "csrc/device_common.h"],
     "bwd_dq_kernel": ["csrc/attn_bwd.hip", "csrc/masks.h", "csrc/device_common.h", "csrc/tile_layout.h"],
     "bwd_dkdv_kernel": ["csrc/attn_bwd.hip", "csrc/masks.h", "csrc/device_common.h", "csrc/tile_layout.h"],
+    "bwd_prep_kernel": ["csrc/attn_bwd.hip", "csrc/masks.h", "csrc/device_common.h", "csrc/tile_layout.h"],
+    "bwd_dqs_kernel": ["csrc/attn_bwd.hip", "csrc/masks.h", "csrc/device_common.h", "csrc/tile_layout.h",
+                       "csrc/launch.h"],
 }
 
 
@@ -51,7 +54,7 @@ def short_name(name: str) -> str:
         return f"decode_partial_kernel<{'bf16' if m.group(1) == 'DF16b' else 'f32'}, {m.group(2)}>"
     m = re.search(r"(fwd_bf16_d128_kernel<[^>]*>|fwd_bf16_kernel<\d+>|fwd_f32_kernel<\d+>|fwd_f32_split_kernel<[^>]*>|"
                   r"decode_partial_kernel\w*|decode_merge_kernel<\d+>|softmax_topk_kernel<\d, (?:true|false)>|"
-                  r"softmax_rows_\w+<[\d, ]+>|bwd_dkdv_kernel|bwd_dq_kernel|fwd_fp8_d128_kernel|"
+                  r"softmax_rows_\w+<[\d, ]+>|bwd_dkdv_kernel(?:<\w+>)?|bwd_dq_kernel|bwd_dqs_kernel|bwd_prep_kernel|fwd_fp8_d128_kernel|"
                   r"__amd_rocclr_copyBuffer|copyBuffer)", name)
     if m:
         return m.group(1)

@@ -27,6 +27,7 @@ int g_syncs = 0;
 hipError_t g_result = hipSuccess;
 osfa::FwdArgs g_fwd{};
 osfa::DecodeArgs g_dec{};
+osfa::BwdArgs g_bwd{};
 int g_fails = 0;
 
 void expect(bool ok, const char* what, int line) {
@@ -49,7 +50,7 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t) { ++g_launches; g
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t) { ++g_launches; g_fwd = a; return g_result; }
 hipError_t launch_attn_fwd_bf16_exp2_offload(const FwdArgs& a, int, hipStream_t) { ++g_launches; g_fwd = a; return g_result; }
 hipError_t launch_attn_fwd_fp8(const FwdArgs& a, float, float, hipStream_t) { ++g_launches; g_fwd = a; return g_result; }
-hipError_t launch_attn_bwd_bf16(const BwdArgs&, hipStream_t) { ++g_launches; return g_result; }
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t) { ++g_launches; g_bwd = a; return g_result; }
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t) { ++g_launches; g_dec = a; return g_result; }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t) { ++g_launches; g_dec = a; return g_result; }
 hipError_t launch_decode_noalloc(const DecodeArgs& a, bool, hipStream_t) { ++g_launches; g_dec = a; return g_result; }
@@ -98,6 +99,22 @@ int main() {
                   attn_bwd_workspace_bytes(1, 2, 300), nullptr) == ATTN_OK);
   EXPECT(attn_bwd(ATTN_BF16, P, P, P, P, P, F, P, P, P, 1, 2, 300, 128, 0.1f, 1, 0, nullptr, P,
                   attn_bwd_workspace_bytes(1, 2, 300) - 1, nullptr) == ATTN_ERR_INVALID_ARG);
+  // The stored-dS way: chosen by the workspace size, tiles after the D / LSE part rounded up to 256 bytes.
+  const size_t bmin = attn_bwd_workspace_bytes(1, 2, 300), bst = attn_bwd_stored_ds_workspace_bytes(1, 2, 300, 1, 0);
+  EXPECT(bst == 4864 + size_t(2) * 10 * 10 * 2048);  // 2*300*4*2 = 4800 -> 4864; 10 query blocks x 10 key blocks
+  EXPECT(attn_bwd(ATTN_BF16, P, P, P, P, P, F, P, P, P, 1, 2, 300, 128, 0.1f, 1, 0, nullptr, P, bmin, nullptr) == ATTN_OK);
+  EXPECT(g_bwd.ds == nullptr);
+  EXPECT(attn_bwd(ATTN_BF16, P, P, P, P, P, F, P, P, P, 1, 2, 300, 128, 0.1f, 1, 0, nullptr, P, bst, nullptr) == ATTN_OK);
+  EXPECT(g_bwd.ds == static_cast<char*>(P) + 4864);
+  EXPECT(attn_bwd(ATTN_BF16, P, P, P, P, P, F, P, P, P, 1, 2, 300, 128, 0.1f, 1, 0, nullptr, P, bst - 1, nullptr) ==
+         ATTN_OK);
+  EXPECT(g_bwd.ds == nullptr);
+  EXPECT(attn_bwd_stored_ds_workspace_bytes(1, 1, 8192, 1, 1024) == 65536 + size_t(256) * 33 * 2048);
+  EXPECT(attn_bwd_stored_ds_workspace_bytes(1, 1, 8192, 0, 1024) == 65536 + size_t(256) * 66 * 2048);
+  EXPECT(attn_bwd_stored_ds_workspace_bytes(1, 1, 100, 1, 5000) == 1024 + size_t(4) * 4 * 2048);  // window > N: clamped
+  EXPECT(attn_bwd_stored_ds_workspace_bytes(1, 1, 1 << 20, 0, 0) == 0);  // one head's tiles > 2^31 bytes
+  EXPECT(attn_bwd_stored_ds_workspace_bytes(0, 1, 8, 0, 0) == 0);
+  EXPECT(attn_bwd_stored_ds_workspace_bytes(1, 1, 8, 2, 0) == 0);
 
   // Decode.
   const size_t ws = attn_decode_splitkv_workspace_bytes(1, 32, 128, 64);

@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_splitkv",
+    for want in ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_bytes",
+                 "attn_bwd_stored_ds_workspace_bytes", "attn_decode_splitkv",
                  "attn_decode_splitkv_workspace_bytes",
                  "online_softmax_rows", "online_softmax_topk_rows", "attn_last_error", "osfa_version"):
         assert want in names
@@ -208,6 +209,20 @@ def test_bwd_rejects(lib, kw, status, msg):
 def test_bwd_workspace_bytes(lib):
     assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 2 * 2 * 3 * 5 * 4
     assert lib.attn_bwd_workspace_bytes(0, 3, 5) == 0
+
+
+def test_bwd_stored_ds_workspace_bytes(lib):
+    """The D / LSE part rounded up to 256 bytes, then one 2 KB tile per (32-query block, visible 32-key block slot)."""
+    f = lib.attn_bwd_stored_ds_workspace_bytes
+    f.argtypes = [ctypes.c_int] * 5
+    f.restype = ctypes.c_size_t
+    # N = 8192: 256 query blocks; causal window 1024 -> 33 key-block slots, non-causal -> 66, none -> 256.
+    assert f(1, 64, 8192, 1, 1024) == 64 * 8192 * 8 + 64 * 256 * 33 * 2048
+    assert f(1, 1, 8192, 0, 1024) == 65536 + 256 * 66 * 2048
+    assert f(1, 1, 8192, 1, 0) == 65536 + 256 * 256 * 2048
+    assert f(2, 1, 100, 1, 5000) == 1792 + 2 * 4 * 4 * 2048  # window clamped to N; 1600 B rounded up to 1792
+    assert f(1, 1, 1 << 20, 0, 0) == 0  # one head's tiles would pass 2^31 bytes
+    assert f(0, 1, 8, 0, 0) == 0 and f(1, 1, 8, 2, 0) == 0 and f(1, 1, 8, 0, -1) == 0
 
 
 @pytest.mark.parametrize("args,msg", [

@@ -15,6 +15,10 @@ accumulation over at most 8192 terms (n 2^-24 < 2^-8 / 7 of the same sums)
 and the float32 error of P = exp2(S log2(e) - LSE log2(e)), ~1e-6 relative.
 Where the bound is 0 (a query that sees no key, a key that no query sees)
 the gradient must be exactly 0.
+
+attn_bwd has two ways to dQ, chosen by the workspace size: storing dS in
+the workspace and multiplying it with K, or recomputing S and dP; the
+parity cases run both.
 """
 import numpy as np
 import pytest
@@ -42,14 +46,24 @@ def assert_grad(got, ref, bound, what):
                              f"ref {ref[i]:.6g} bound {bound[i]:.3e}; normwise {err.max() / max(np.abs(ref).max(), 1e-300):.3e}")
 
 
-def run_fwd_bwd(inp, do_bits):
+def ws_bytes(B, H, N, causal, window, stored):
+    """Workspace for the stored-dS way (which must apply) or the minimum (dQ recomputes S and dP)."""
+    need = osfa.bwd_workspace_bytes(B, H, N)
+    if stored:
+        st = osfa.bwd_stored_ds_workspace_bytes(B, H, N, causal, window)
+        assert st > need
+        need = st
+    return need
+
+
+def run_fwd_bwd(inp, do_bits, stored=True):
     q, k, v = upload_bf16(inp.q_bits), upload_bf16(inp.k_bits), upload_bf16(inp.v_bits)
     dout = upload_bf16(do_bits)
     B, H, N, d = inp.q.shape
     kvl = None if inp.kv_len is None else torch.from_numpy(inp.kv_len).to("cuda:0")
     o, lse = osfa.attn_fwd(q, k, v, scale=inp.scale, causal=inp.causal, window=inp.window, kv_len=kvl)
     grads = [Guarded((B, H, N, d), torch.bfloat16) for _ in range(3)]
-    ws = Guarded((max(osfa.bwd_workspace_bytes(B, H, N) // 4, 1),), torch.float32)
+    ws = Guarded(((ws_bytes(B, H, N, inp.causal, inp.window, stored) + 3) // 4,), torch.float32)
     osfa.attn_bwd(q, k, v, o, dout, lse, scale=inp.scale, causal=inp.causal, window=inp.window, kv_len=kvl,
                   dq=grads[0].t, dk=grads[1].t, dv=grads[2].t, workspace=ws.t)
     torch.cuda.synchronize()
@@ -100,15 +114,33 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("stored", [True, False], ids=["stored_ds", "recompute"])
 @pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
-def test_bwd_parity(case):
+def test_bwd_parity(case, stored):
     B, H, N, causal, window, kv_len, nbig = case
-    print(f"attn_bwd bf16 B={B} H={H} N={N} d=128 causal={causal} window={window} kv_len={kv_len}", flush=True)
+    print(f"attn_bwd bf16 B={B} H={H} N={N} d=128 causal={causal} window={window} kv_len={kv_len} stored={stored}",
+          flush=True)
     inp = attn_inputs(B, H, N, 128, dtype="bf16", seed=N + B + 7, causal=causal, window=window, kv_len=kv_len,
                       n_big_keys=nbig)
     do_bits, do = grad_inputs(B, H, N, 128, seed=N + 3)
-    got = run_fwd_bwd(inp, do_bits)
+    got = run_fwd_bwd(inp, do_bits, stored)
     check(inp, do, got)
+
+
+@pytest.mark.parametrize("case", [CASES[7], CASES[8], CASES[12]], ids=["window_pad", "noncausal_window", "wide"])
+def test_bwd_paths_agree(case):
+    """dK and dV come from the same kernel either way (identical); dQ from the stored dS or from recomputed S and
+    dP, which form dS the same way."""
+    B, H, N, causal, window, kv_len, nbig = case
+    inp = attn_inputs(B, H, N, 128, dtype="bf16", seed=N + 11, causal=causal, window=window, kv_len=kv_len,
+                      n_big_keys=nbig)
+    do_bits, do = grad_inputs(B, H, N, 128, seed=N + 5)
+    a = run_fwd_bwd(inp, do_bits, True)
+    r = run_fwd_bwd(inp, do_bits, False)
+    assert np.array_equal(a[1], r[1]) and np.array_equal(a[2], r[2])
+    print(f"dQ identical across the two ways: {np.array_equal(a[0], r[0])}; max diff {np.abs(a[0] - r[0]).max():.3e}",
+          flush=True)
+    check(inp, do, a)
 
 
 def test_bwd_self_only():
@@ -120,12 +152,12 @@ def test_bwd_self_only():
     assert np.abs(dq).max() <= 1e-3 and np.abs(dk).max() <= 1e-3
 
 
-def _full(name, heads):
+def _full(name, heads, stored=True):
     w = WORKLOADS[name]
-    print(f"attn_bwd full workload {name}", flush=True)
+    print(f"attn_bwd full workload {name} stored={stored}", flush=True)
     inp = workload_attn_inputs(name)
     do_bits, do = grad_inputs(w["B"], w["H"], w["N"], w["d"], seed=w["seed"])
-    got = run_fwd_bwd(inp, do_bits)
+    got = run_fwd_bwd(inp, do_bits, stored)
     for g in got:
         assert np.isfinite(g).all()
     check(inp, do, got, heads=heads)
@@ -135,8 +167,9 @@ def test_bwd_full_bf16_causal_2048():
     _full("attn_bf16_causal_b4h32_n2048_d128", heads=[(0, 0), (2, 13), (3, 31)])
 
 
-def test_bwd_full_bf16_window_pad_8192():
-    _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0), (0, 63)])
+@pytest.mark.parametrize("stored", [True, False], ids=["stored_ds", "recompute"])
+def test_bwd_full_bf16_window_pad_8192(stored):
+    _full("attn_bf16_causal_w1024_pad512_b1h64_n8192_d128", heads=[(0, 0), (0, 63)], stored=stored)
 
 
 def test_bwd_largest_offsets():
@@ -160,7 +193,7 @@ def test_bwd_largest_offsets():
     kv = torch.tensor([kvl], dtype=torch.int32, device="cuda:0")
     o, lse = osfa.attn_fwd(q, k, v, scale=scale, causal=True, window=W, kv_len=kv)
     grads = [Guarded((B, H, N, d), torch.bfloat16) for _ in range(3)]
-    ws = Guarded((osfa.bwd_workspace_bytes(B, H, N) // 4,), torch.float32)
+    ws = Guarded(((ws_bytes(B, H, N, True, W, True) + 3) // 4,), torch.float32)  # the stored-dS way
     osfa.attn_bwd(q, k, v, o, dout, lse, scale=scale, causal=True, window=W, kv_len=kv, dq=grads[0].t,
                   dk=grads[1].t, dv=grads[2].t, workspace=ws.t)
     torch.cuda.synchronize()
