@@ -601,19 +601,17 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // Stored-dS path.  bwd_dkdv_kernel also writes each visible block's dS (the
 // tiles of launch.h), and dQ = scale dS K becomes a product over the stored
-// tiles instead of a second pass computing S and dP: 6d FLOPs per visible
+// tiles instead of a second pass computing S and dP: 4d FLOPs per visible
 // pair fewer.  D and LSE log2(e), which bwd_dkdv_kernel needs first, come
 // from bwd_prep_kernel.
 // ---------------------------------------------------------------------------
 
 // D_i = sum_d dO_id O_id and LSE_i log2(e) (+inf for a row with no key): the
 // lanes, products and sums of bwd_dq_kernel's prologue, so both paths use the
-// same values.  The tile's O and dO rows come in by coalesced buffer loads to
-// LDS (the swizzled block layout), and each lane then reads its 16-byte
-// pieces from there in bwd_dq_kernel's order.
+// same values.  Each lane loads its own 16-byte pieces of O and dO (piece
+// 2 kk + hf of its row, the piece bwd_dq_kernel reads from LDS for kk) and
+// sums them in that order; no LDS, so many waves per CU keep loads in flight.
 __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char ol[kTile * D * 2];  // 32 KB
-  __shared__ __attribute__((aligned(1024))) char gl[kTile * D * 2];
   const Tile tile = map_tile(p, false);
   if (!tile.valid) return;
   const int N = p.N;
@@ -623,23 +621,24 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdParams p) {
   const size_t head = (size_t)tile.bh * N;
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)(p.o + head * D), 0, N * D * 2, kBufDword3);
   const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + head * D), 0, N * D * 2, kBufDword3);
-  // Rows past N read row N - 1 (not stored below).
-  stage_rows<kTile / 4>(ors, ol, tile.t0, N, w, lane);
-  stage_rows<kTile / 4>(grs, gl, tile.t0, N, w, lane);
   const int qi = tile.t0 + 32 * w + l32;
   const bool qok = qi < N;
+  const int row = qok ? qi : N - 1;  // rows past N read row N - 1 (not stored below)
+  u32x4 a[NKK], g[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int off = (row * D + 8 * (2 * kk + hf)) * 2;
+    a[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, off, 0, 0));
+    g[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
+  }
   const float lse_in = qok ? p.lse[head + qi] : kNegInf;
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
   float dlt = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    const u32x4 a = __builtin_bit_cast(u32x4, row_frag(ol, 32 * w + l32, kk, hf));
-    const u32x4 g = __builtin_bit_cast(u32x4, row_frag(gl, 32 * w + l32, kk, hf));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dlt = fmaf(bf16_lo(a[e]), bf16_lo(g[e]), dlt);
-      dlt = fmaf(bf16_hi(a[e]), bf16_hi(g[e]), dlt);
+      dlt = fmaf(bf16_lo(a[kk][e]), bf16_lo(g[kk][e]), dlt);
+      dlt = fmaf(bf16_hi(a[kk][e]), bf16_hi(g[kk][e]), dlt);
     }
   }
   dlt = sum_halves(dlt);
@@ -730,11 +729,13 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p)
                (row / kDsTile) * (kDsTile * kDsTile * 2);
   }
   u32x4 kr[kDqsRing][KLOADS], sr[kDqsRing][SLOADS];
+  // A block at or past nblk (the ring runs up to three ahead) loads from
+  // past the end of the buffer: zeros, with no memory access to wait for.
   auto load_k = [&](int j, int t) {
     const int row = 4 * (w + kDqsWaves * t) + (lane >> 4);
     const int grow = min((kb_lo + j) * kBc + row, N - 1);
-    return __builtin_bit_cast(u32x4,
-                              __builtin_amdgcn_raw_buffer_load_b128(krs, (grow * D + 8 * ((lane & 15) ^ swz(row))) * 2, 0, 0));
+    const int off = j < nblk ? (grow * D + 8 * ((lane & 15) ^ swz(row))) * 2 : N * D * 2;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
   };
   auto load_s = [&](int j, int t) {
     const int j0 = (kb_lo + j) * kBc;
@@ -866,21 +867,32 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p)
     }
   }
 
+  // dQ rows through LDS: a lane holds 8-byte pieces of one query row
+  // (elements 32 md + 8 rq + 4 hf .. + 3), which stored directly would be
+  // 16-byte runs scattered over 32 rows per instruction.  Each wave writes
+  // its 64 rows (16 KB, swizzled block layout) to a region of its own, past
+  // the loop's last barrier, and stores them back as whole 256-byte rows.
+  static_assert(kDqsWaves == 4 && 32 * kDqsQg * D * 2 * 2 == 2 * BLK, "two 64-row regions per LDS stage");
+  char* reg = (w < 2 ? s0 : s1) + (w & 1) * (32 * kDqsQg * D * 2);
 #pragma unroll
-  for (int qg = 0; qg < kDqsQg; ++qg) {
-    const int qi = qa + 32 * qg + l32;
-    if (qi < N) {
-      __bf16* dst = p.dq + (head + qi) * D;
+  for (int qg = 0; qg < kDqsQg; ++qg)
 #pragma unroll
-      for (int md = 0; md < NMD; ++md)
+    for (int md = 0; md < NMD; ++md)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          u32x2 wv;
-          wv[0] = pack_bf16x2(acc[qg][md][4 * rq + 0] * p.scale, acc[qg][md][4 * rq + 1] * p.scale);
-          wv[1] = pack_bf16x2(acc[qg][md][4 * rq + 2] * p.scale, acc[qg][md][4 * rq + 3] * p.scale);
-          *reinterpret_cast<u32x2*>(dst + 32 * md + 8 * rq + 4 * hf) = wv;
-        }
-    }
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 wv;
+        wv[0] = pack_bf16x2(acc[qg][md][4 * rq + 0] * p.scale, acc[qg][md][4 * rq + 1] * p.scale);
+        wv[1] = pack_bf16x2(acc[qg][md][4 * rq + 2] * p.scale, acc[qg][md][4 * rq + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(reg + kv_off(32 * qg + l32, 4 * md + rq) + 8 * hf) = wv;
+      }
+  constexpr int NT = 32 * kDqsQg / 4;  // 4 rows per instruction
+  u32x4 rows[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) rows[t] = *reinterpret_cast<const u32x4*>(reg + kv_off(4 * t + (lane >> 4), lane & 15));
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int qi = qa + 4 * t + (lane >> 4);
+    if (qi < N) *reinterpret_cast<u32x4*>(p.dq + (head + qi) * D + 8 * (lane & 15)) = rows[t];
   }
 }
 

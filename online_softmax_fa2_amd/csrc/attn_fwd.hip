@@ -744,21 +744,36 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_d128_kernel(FwdParams p) 
   const float l_tot = sum_halves(l_run);
   const float l_div = sum_halves(l_bf);
   const float inv = l_div > 0.0f ? 1.0f / l_div : 0.0f;
-  if (qi < N) {
-    __bf16* Og = static_cast<__bf16*>(p.o) + head_off + (size_t)qi * D;
+  // O rows through LDS: a lane holds 8-byte pieces of one row (columns
+  // 32 md + 8 rq + 4 hf .. + 3), which stored directly would be 16-byte runs
+  // scattered over 32 rows per instruction.  Once every wave is past its
+  // last K/V read and no load to LDS is in flight, each wave writes its 32
+  // rows (8 KB, swizzled block layout) to its own part of the K buffers and
+  // stores them back as whole 256-byte rows.
+  static_assert(NW * 32 * D * 2 <= 2 * BLK && NW % 2 == 0, "the O rows fit in the two K buffers");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  char* orow = (w < NW / 2 ? k0 : k1) + (w % (NW / 2)) * (32 * D * 2);
 #pragma unroll
-    for (int md = 0; md < NMD; ++md)
+  for (int md = 0; md < NMD; ++md)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int dcol = 32 * md + 8 * rq + 4 * hf;
-        u32x2 wv;
-        wv[0] = pack_bf16x2(oacc[md][4 * rq + 0] * inv, oacc[md][4 * rq + 1] * inv);
-        wv[1] = pack_bf16x2(oacc[md][4 * rq + 2] * inv, oacc[md][4 * rq + 3] * inv);
-        *reinterpret_cast<u32x2*>(Og + dcol) = wv;
-      }
-    if (hf == 0)
-      p.lse[(size_t)tile.bh * N + qi] = l_tot > 0.0f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    for (int rq = 0; rq < 4; ++rq) {
+      u32x2 wv;
+      wv[0] = pack_bf16x2(oacc[md][4 * rq + 0] * inv, oacc[md][4 * rq + 1] * inv);
+      wv[1] = pack_bf16x2(oacc[md][4 * rq + 2] * inv, oacc[md][4 * rq + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + kv_off(l32, 4 * md + rq) + 8 * hf) = wv;
+    }
+  u32x4 rows[8];  // 4 rows per instruction
+#pragma unroll
+  for (int t = 0; t < 8; ++t) rows[t] = *reinterpret_cast<const u32x4*>(orow + kv_off(4 * t + (lane >> 4), lane & 15));
+  __bf16* Og = static_cast<__bf16*>(p.o) + head_off;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int qr = q0 + 32 * w + 4 * t + (lane >> 4);
+    if (qr < N) *reinterpret_cast<u32x4*>(Og + (size_t)qr * D + 8 * (lane & 15)) = rows[t];
   }
+  if (qi < N && hf == 0)
+    p.lse[(size_t)tile.bh * N + qi] = l_tot > 0.0f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
