@@ -175,6 +175,34 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* blk, const TrOff& t, int m
   return __builtin_bit_cast(bf16x8, hv);
 }
 
+// A wave's 32 output rows of 128 bf16 (lane: row l32, columns 32 md + 8 rq
+// + 4 hf .. + 3 from a[md][4 rq .. 4 rq + 3], times f) stored as whole
+// 256-byte rows r0 .. r0 + 31 of dst, rows >= nrows skipped.  Stored
+// directly, each instruction would write 16-byte runs scattered over 32
+// rows; the rows go through `reg`, 8 KB of LDS that only this wave uses
+// (swizzled block layout), and back out 4 rows per instruction.
+__device__ __forceinline__ void store_rows(char* reg, const f32x16 (&a)[NMD], float f, __bf16* dst, int r0, int nrows,
+                                           int lane) {
+  const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      u32x2 wv;
+      wv[0] = pack_bf16x2(a[md][4 * rq + 0] * f, a[md][4 * rq + 1] * f);
+      wv[1] = pack_bf16x2(a[md][4 * rq + 2] * f, a[md][4 * rq + 3] * f);
+      *reinterpret_cast<u32x2*>(reg + kv_off(l32, 4 * md + rq) + 8 * hf) = wv;
+    }
+  u32x4 rows[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) rows[t] = *reinterpret_cast<const u32x4*>(reg + kv_off(4 * t + (lane >> 4), lane & 15));
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int r = r0 + 4 * t + (lane >> 4);
+    if (r < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)r * D + 8 * (lane & 15)) = rows[t];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dQ: query tiles of 128, key blocks of 64.
 // ---------------------------------------------------------------------------
@@ -341,18 +369,11 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   }
   if (j < nblk) iter(j, k0, v0, k1, v1);
 
-  if (qok) {
-    __bf16* dst = p.dq + (head + qi) * D;
-#pragma unroll
-    for (int md = 0; md < NMD; ++md)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        u32x2 wv;
-        wv[0] = pack_bf16x2(acc[md][4 * rq + 0] * p.scale, acc[md][4 * rq + 1] * p.scale);
-        wv[1] = pack_bf16x2(acc[md][4 * rq + 2] * p.scale, acc[md][4 * rq + 3] * p.scale);
-        *reinterpret_cast<u32x2*>(dst + 32 * md + 8 * rq + 4 * hf) = wv;
-      }
-  }
+  // dQ rows through the K buffers, once every wave is past its last read.
+  static_assert(kW == 4, "two waves' rows per K buffer");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  store_rows((w < 2 ? k0 : k1) + (w & 1) * (32 * D * 2), acc, p.scale, p.dq + head * D, tile.t0 + 32 * w, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -581,21 +602,12 @@ __global__ __launch_bounds__(kT, 2) void bwd_dkdv_kernel(BwdParams p) {
   // No load into LDS may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  auto store = [&](__bf16* dst, const f32x16 (&a)[NMD], float f) {
-#pragma unroll
-    for (int md = 0; md < NMD; ++md)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        u32x2 wv;
-        wv[0] = pack_bf16x2(a[md][4 * rq + 0] * f, a[md][4 * rq + 1] * f);
-        wv[1] = pack_bf16x2(a[md][4 * rq + 2] * f, a[md][4 * rq + 3] * f);
-        *reinterpret_cast<u32x2*>(dst + 32 * md + 8 * rq + 4 * hf) = wv;
-      }
-  };
-  if (kj < N) {
-    store(p.dk + (head + kj) * D, acck, p.scale);
-    store(p.dv + (head + kj) * D, accv, 1.0f);
-  }
+  // dK, then dV, rows through this wave's quarter of the V tile, once every
+  // wave is past its last read of it.
+  __syncthreads();
+  char* reg = vtile + w * (32 * D * 2);
+  store_rows(reg, acck, p.scale, p.dk + head * D, k0 + 32 * w, N, lane);
+  store_rows(reg, accv, 1.0f, p.dv + head * D, k0 + 32 * w, N, lane);
 }
 
 // ---------------------------------------------------------------------------
