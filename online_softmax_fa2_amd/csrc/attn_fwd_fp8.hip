@@ -249,19 +249,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_d128_kernel(FwdParams p) 
   const float lq = __shfl(lacc[0], l32, 64);
   const float l_tot = sum_halves(l_run);
   const float inv = lq > 0.0f ? p.o_scale / lq : 0.0f;
-  if (qok) {
-    __bf16* Og = static_cast<__bf16*>(p.o) + (head + qi) * kD8;
+  // O rows through LDS: a lane holds 8-byte pieces of one bf16 row (columns
+  // 32 md + 8 rq + 4 hf .. + 3), which stored directly would be 16-byte runs
+  // scattered over 32 rows per instruction.  Once every wave is past its
+  // last K/V read and no load to LDS is in flight, each wave writes its 32
+  // rows (8 KB, the 256-byte-row swizzle of tile_layout.h) to one of the four
+  // K/V buffers and stores them back as whole rows.
+  static_assert(kThreads == 256 && kBlk8 == 32 * kD8 * 2, "one 8 KB buffer per wave");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  char* orow = w == 0 ? k0 : w == 1 ? k1 : w == 2 ? v0 : v1;
 #pragma unroll
-    for (int md = 0; md < 4; ++md)
+  for (int md = 0; md < 4; ++md)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        u32x2 wv;
-        wv[0] = pack_bf16x2(oacc[md][4 * rq + 0] * inv, oacc[md][4 * rq + 1] * inv);
-        wv[1] = pack_bf16x2(oacc[md][4 * rq + 2] * inv, oacc[md][4 * rq + 3] * inv);
-        *reinterpret_cast<u32x2*>(Og + 32 * md + 8 * rq + 4 * hf) = wv;
-      }
-    if (hf == 0) p.lse[head + qi] = l_tot > 0.0f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    for (int rq = 0; rq < 4; ++rq) {
+      u32x2 wv;
+      wv[0] = pack_bf16x2(oacc[md][4 * rq + 0] * inv, oacc[md][4 * rq + 1] * inv);
+      wv[1] = pack_bf16x2(oacc[md][4 * rq + 2] * inv, oacc[md][4 * rq + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + kv_off(l32, 4 * md + rq) + 8 * hf) = wv;
+    }
+  u32x4 rows[8];  // 4 rows per instruction
+#pragma unroll
+  for (int t = 0; t < 8; ++t) rows[t] = *reinterpret_cast<const u32x4*>(orow + kv_off(4 * t + (lane >> 4), lane & 15));
+  __bf16* Og = static_cast<__bf16*>(p.o) + head * kD8;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int qr = q0 + 32 * w + 4 * t + (lane >> 4);
+    if (qr < N) *reinterpret_cast<u32x4*>(Og + (size_t)qr * kD8 + 8 * (lane & 15)) = rows[t];
   }
+  if (qok && hf == 0) p.lse[head + qi] = l_tot > 0.0f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
 }
 
 }  // namespace
