@@ -185,12 +185,19 @@ def bwd_stored_ds_workspace_bytes(B: int, H: int, N: int, causal: bool = False, 
     return int(load_library().attn_bwd_stored_ds_workspace_bytes(B, H, N, int(bool(causal)), int(window)))
 
 
+# Largest workspace attn_bwd allocates by itself to store dS; beyond it (or beyond a quarter of the free
+# device memory) it takes the minimum workspace and recomputes.  dS takes 2 bytes per visible pair, which
+# without a window grows as N^2.
+STORED_DS_MAX_BYTES = 8 << 30
+
+
 def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False, window: int = 0,
              kv_len=None, dq=None, dk=None, dv=None, workspace=None, stream=None, stored_ds: bool = True):
     """(dQ, dK, dV) of attention for [B, H, N, d] bf16 tensors, given O and LSE from attn_fwd.
 
-    Without a `workspace`, one is allocated: large enough to store dS (the faster way) when `stored_ds` and
-    that way applies, else the minimum (dQ recomputes S and dP).  A given workspace decides by its size.
+    Without a `workspace`, one is allocated: large enough to store dS (the faster way) when `stored_ds`,
+    that way applies and it needs at most STORED_DS_MAX_BYTES and a quarter of the free device memory;
+    else the minimum (dQ recomputes S and dP).  A given workspace decides by its size.
     """
     if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, o, dout)):
         raise ValueError("q, k, v, o, dout must share one dtype")
@@ -212,8 +219,10 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = F
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     need = bwd_workspace_bytes(B, H, N)
-    if stored_ds:
-        need = max(need, bwd_stored_ds_workspace_bytes(B, H, N, causal, window))
+    if stored_ds and workspace is None:
+        st = bwd_stored_ds_workspace_bytes(B, H, N, causal, window)
+        if 0 < st <= STORED_DS_MAX_BYTES and st <= torch.cuda.mem_get_info(q.device)[0] // 4:
+            need = max(need, st)
     if workspace is None:
         workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
     _need_device(q, k, v, o, dout, lse, kv_len, dq, dk, dv, workspace)

@@ -143,6 +143,28 @@ def test_bwd_paths_agree(case):
     check(inp, do, a)
 
 
+def test_bwd_default_workspace_choice(monkeypatch):
+    """Without a workspace the binding picks the way by size: the stored-dS way by default, the recomputing
+    way with stored_ds=False or when the stored workspace exceeds its cap; the three give the same gradients
+    (bit for bit: both ways form dS alike and accumulate in the same order)."""
+    from online_softmax_fa2_amd import _binding
+    inp = attn_inputs(1, 2, 300, 128, dtype="bf16", seed=91, causal=True, window=70)
+    do_bits, do = grad_inputs(1, 2, 300, 128, seed=92)
+    q, k, v = upload_bf16(inp.q_bits), upload_bf16(inp.k_bits), upload_bf16(inp.v_bits)
+    dout = upload_bf16(do_bits)
+    o, lse = osfa.attn_fwd(q, k, v, scale=inp.scale, causal=True, window=70)
+    print("attn_bwd default workspace: B=1 H=2 N=300 causal window=70", flush=True)
+    outs = [osfa.attn_bwd(q, k, v, o, dout, lse, scale=inp.scale, causal=True, window=70)]
+    outs.append(osfa.attn_bwd(q, k, v, o, dout, lse, scale=inp.scale, causal=True, window=70, stored_ds=False))
+    monkeypatch.setattr(_binding, "STORED_DS_MAX_BYTES", 0)
+    outs.append(osfa.attn_bwd(q, k, v, o, dout, lse, scale=inp.scale, causal=True, window=70))
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
+    check(inp, do, [g.float().cpu().numpy() for g in outs[0]])
+
+
 def test_bwd_self_only():
     """Causal window 1: P = 1 on the diagonal, so dV = dO exactly and dS = 0 (dQ, dK vanish up to rounding)."""
     inp = attn_inputs(1, 2, 300, 128, dtype="bf16", seed=93, causal=True, window=1)
