@@ -661,34 +661,36 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// dQ^T += K^T dS^T over the stored tiles.  A workgroup of 4 waves (one per
-// CU, one wave per SIMD) owns 256 queries, 64 per wave, and walks its key
-// range in blocks of 64.  The operands come from LDS: K^T (transposed reads
-// of the K block, the same for every wave) and dS^T (transposed reads of the
-// wave's own queries).  What one wave reads per MFMA sets the LDS traffic,
-// and with 64 queries a wave reads each K^T fragment once for two MFMAs:
-// 24 KB of reads per wave for 32 MFMAs per block.  The stored dS is
-// streamed from HBM once, by non-temporal loads that leave K in L2.  Each
-// wave holds its 12 16-byte pieces of the next two blocks (K rows, then dS)
-// in a ring of registers; while it multiplies block j it writes block j + 1
-// from the ring to the other LDS stage (the swizzled block layout: K, then
-// dS for queries 0..127 and 128..255), one piece per MFMA pair, and reloads
-// each piece's registers with block j + 3.  A tile no query of its block
-// sees is loaded from past the end of the buffer and reads as zeros.  Every
-// accumulator takes its key groups in the order of bwd_dq_kernel.
+// dQ^T += K^T dS^T over the stored tiles.  A workgroup of 4 waves owns
+// kDqsTile queries, 32 kDqsQg per wave, and walks its key range in blocks of
+// 64.  The operands come from LDS: K^T (transposed reads of the K block, the
+// same for every wave) and dS^T (transposed reads of the wave's own
+// queries).  With kDqsQg = 2 a wave reads each K^T fragment once for two
+// MFMAs but the workgroup is alone on its CU (96 KB of LDS, one wave per
+// SIMD); kDqsQg = 1 runs two workgroups per CU, whose prologues and
+// epilogues overlap the other's loop, which measured faster.  The stored
+// dS is streamed from HBM once, by non-temporal loads that leave K in L2.
+// Each wave holds its 16-byte pieces of the next two blocks (K rows, then
+// dS) in a ring of registers; while it multiplies block j it writes block
+// j + 1 from the ring to the other LDS stage (the swizzled block layout: K,
+// then dS for queries 0..127 (and 128..255)), one piece per MFMA pair, and
+// reloads each piece's registers with block j + 3.  A tile no query of its
+// block sees is loaded from past the end of the buffer and reads as zeros.
+// Every accumulator takes its key groups in the order of bwd_dq_kernel.
 constexpr int kDqsWaves = 4;
-constexpr int kDqsQg = 2;                          // 32-query groups per wave
+constexpr int kDqsQg = 1;                          // 32-query groups per wave
 constexpr int kDqsTile = 32 * kDqsQg * kDqsWaves;  // queries per workgroup
 constexpr int kDqsRing = 2;                        // ring slots (blocks) per wave
-__global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p) {
-  constexpr int BLK = kBc * D * 2;        // 16 KB
-  constexpr int KLOADS = 16 / kDqsWaves;  // 16-byte K pieces per lane per block
-  constexpr int SLOADS = 32 / kDqsWaves;  // 16-byte dS pieces per lane per block
-  constexpr int AHEAD = 4;                // K^T fragments in flight
-  static_assert(kDqsTile == 256, "two LDS halves of 128 queries");
-  // Two LDS stages of (K block, dS for queries 0..127, dS for 128..255).
+constexpr int kDqsHalves = kDqsTile / 128;         // LDS dS halves of 128 queries
+__global__ __launch_bounds__(64 * kDqsWaves, 3 - kDqsHalves) void bwd_dqs_kernel(BwdParams p) {
+  constexpr int BLK = kBc * D * 2;                      // 16 KB
+  constexpr int KLOADS = 16 / kDqsWaves;                // 16-byte K pieces per lane per block
+  constexpr int SLOADS = 16 * kDqsHalves / kDqsWaves;   // 16-byte dS pieces per lane per block
+  constexpr int AHEAD = 4;                              // K^T fragments in flight
+  static_assert(kDqsHalves == 1 || kDqsHalves == 2, "one or two LDS halves of 128 queries");
+  // Two LDS stages of (K block, dS for queries 0..127 (, 128..255)).
   __shared__ __attribute__((aligned(1024))) char k0[BLK], k1[BLK];
-  __shared__ __attribute__((aligned(1024))) char s0[2 * BLK], s1[2 * BLK];
+  __shared__ __attribute__((aligned(1024))) char s0[kDqsHalves * BLK], s1[kDqsHalves * BLK];
 
   const Tile tile = map_tile(p, false, kDqsTile);
   if (!tile.valid) return;
@@ -701,7 +703,7 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p)
   const size_t head = (size_t)tile.bh * N;
   const int jmax = key_limit(p, b);
 
-  // Key range of the tile (as bwd_dq_kernel, for 256 queries).
+  // Key range of the tile (as bwd_dq_kernel, for its kDqsTile queries).
   int kend = jmax;
   if (p.causal) kend = min(kend, q0 + kDqsTile);
   if (p.window > 0 && !p.causal) kend = min(kend, q0 + kDqsTile - 1 + p.window);
@@ -778,8 +780,9 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p)
 
   const int qa = q0 + 32 * kDqsQg * w, qz = qa + 32 * kDqsQg - 1;
   const TrOff tro = tr_offsets(lane);
-  // dS^T read offsets of query group qg of the wave: queries 64 w + 32 qg of
-  // the tile are column group 2 (w % 2) + qg of half w / 2.
+  // dS^T read offsets of query group qg of the wave: queries
+  // o = 32 (kDqsQg w + qg) of the tile are column group (o / 32) % 4 of
+  // half o / 128.
   int soff[kDqsQg][2];
   {
     const int tr_g = lane >> 4, tr_j = lane & 15;
@@ -789,7 +792,8 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p)
     for (int qg = 0; qg < kDqsQg; ++qg)
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        soff[qg][r] = (w >> 1) * BLK + kv_off(4 * r + rowoff, (32 * (2 * (w & 1) + qg) + col) >> 3) + (tr_j & 1) * 8;
+        soff[qg][r] = ((kDqsQg * w + qg) >> 2) * BLK + kv_off(4 * r + rowoff, (32 * ((kDqsQg * w + qg) & 3) + col) >> 3) +
+                      (tr_j & 1) * 8;
   }
   auto sfrag = [&](const char* blk, int qg, int g) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -882,9 +886,10 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_kernel(BwdParams p)
   // dQ rows through LDS: a lane holds 8-byte pieces of one query row
   // (elements 32 md + 8 rq + 4 hf .. + 3), which stored directly would be
   // 16-byte runs scattered over 32 rows per instruction.  Each wave writes
-  // its 64 rows (16 KB, swizzled block layout) to a region of its own, past
-  // the loop's last barrier, and stores them back as whole 256-byte rows.
-  static_assert(kDqsWaves == 4 && 32 * kDqsQg * D * 2 * 2 == 2 * BLK, "two 64-row regions per LDS stage");
+  // its rows (32 per query group, swizzled block layout) to a region of its
+  // own, past the loop's last barrier, and stores them back as whole
+  // 256-byte rows.
+  static_assert(kDqsWaves == 4 && 32 * kDqsQg * D * 2 * 2 == kDqsHalves * BLK, "two wave regions per LDS stage");
   char* reg = (w < 2 ? s0 : s1) + (w & 1) * (32 * kDqsQg * D * 2);
 #pragma unroll
   for (int qg = 0; qg < kDqsQg; ++qg)
