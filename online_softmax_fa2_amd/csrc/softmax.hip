@@ -24,8 +24,8 @@ namespace {
 
 constexpr int kSmThreads = 256;
 constexpr int kSmWaves = kSmThreads / 64;
-// Rows of at most 4096 aligned floats, at least 16 per CU: one wave per row
-// (else a workgroup per row).
+// Rows of at most 4096 aligned floats, at least 16 per CU: one wave per row,
+// or per two rows of more than 2048 floats (else a workgroup per row).
 constexpr bool kSoftmaxWavePerRow = true;
 
 // Element access, 4-wide when the row allows it.  ld/st go through the
@@ -125,45 +125,60 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_reg_kernel(const floa
   }
 }
 
-// Rows of up to 64 x VPT 4-float accesses, one wave per row (4 rows per
-// workgroup): lane l owns accesses l + 64 i, the pair is merged across the
-// wave only (no LDS, no barrier), and a launch over a few thousand rows has
-// every row's loads in flight at once instead of a workgroup per row in two
-// rounds.
-template <int VPT>
+// Rows of up to 64 x VPT 4-float accesses, one wave per row (or per R rows):
+// lane l owns accesses l + 64 i, the pair is merged across the wave only (no
+// LDS, no barrier), and a launch over a few thousand rows has every row's
+// loads in flight at once instead of a workgroup per row in two rounds.
+// With R = 2 a wave takes rows g and g + ceil(rows / 2) and issues the loads
+// of both before it reduces the first, so the first row's stores overlap the
+// second row's loads.
+template <int VPT, int R>
 __global__ __launch_bounds__(kSmThreads) void softmax_rows_wave_kernel(const float* x, float* y, int rows, int cols) {
-  const int row = blockIdx.x * kSmWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int g = blockIdx.x * kSmWaves + (threadIdx.x >> 6);
+  const int per = (rows + R - 1) / R;  // rows per slot s: row g + per s
+  if (g >= per) return;
   const int lane = threadIdx.x & 63;
-  const float* xr = x + (size_t)row * cols;
-  float* yr = y + (size_t)row * cols;
   const int nacc = cols / 4;
-  float v[VPT][4];
-  float mx = kNegInf;
+  float v[R][VPT][4];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int a = lane + 64 * i;
-    if (a < nacc) {
-      ld_nt<4>(xr + (size_t)a * 4, v[i]);
-    } else {
+  for (int s = 0; s < R; ++s) {
+    // A slot past the last row loads row g again and is not used.
+    const int row = g + per * s < rows ? g + per * s : g;
+    const float* xr = x + (size_t)row * cols;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[i][e] = kNegInf;
+    for (int i = 0; i < VPT; ++i) {
+      const int a = lane + 64 * i;
+      ld_nt<4>(xr + (size_t)(a < nacc ? a : 0) * 4, v[s][i]);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, v[i][e]);
   }
-  MD r{kNegInf, 0.0f};
-  fold_chunk(r, mx, &v[0][0], VPT * 4);  // -inf slots contribute exp2(-inf) = 0
-  r = wave_md_merge(r);
-  const float inv = 1.0f / r.d;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int a = lane + 64 * i;
-    if (a < nacc) {
-      float o[4];
+  for (int s = 0; s < R; ++s) {
+    const int row = g + per * s;
+    if (row >= rows) break;  // wave-uniform
+    float mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = fast_exp2(fmaf(v[i][e], kLog2e, -r.m)) * inv;
-      st_nt<4>(yr + (size_t)a * 4, o);
+    for (int i = 0; i < VPT; ++i) {
+      const bool ok = lane + 64 * i < nacc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[s][i][e] = ok ? v[s][i][e] : kNegInf;
+        mx = fmaxf(mx, v[s][i][e]);
+      }
+    }
+    MD r{kNegInf, 0.0f};
+    fold_chunk(r, mx, &v[s][0][0], VPT * 4);  // -inf slots contribute exp2(-inf) = 0
+    r = wave_md_merge(r);
+    const float inv = 1.0f / r.d;
+    float* yr = y + (size_t)row * cols;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int a = lane + 64 * i;
+      if (a < nacc) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fast_exp2(fmaf(v[s][i][e], kLog2e, -r.m)) * inv;
+        st_nt<4>(yr + (size_t)a * 4, o);
+      }
     }
   }
 }
@@ -245,10 +260,14 @@ __device__ __forceinline__ float unord_f(int b) { return __builtin_bit_cast(floa
 // first pass keeps x in the caches); without it x is read once, non-temporal.
 // (Two instantiations: with a run-time test the compiler merges the two
 // loads into one and drops the non-temporal hint.)
+// A chunk is U = 2 accesses per thread (8 KB for the workgroup in float4):
+// two chunks in flight per workgroup measured faster than 16 KB chunks (less
+// work between a chunk's arrival and the next load) and than three chunks
+// in flight.
 template <int W, bool WITH_Y>
 __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x, float* y, float* topv,
                                                                    int32_t* topi, int cols, int k) {
-  constexpr int U = 4;
+  constexpr int U = 2;
   constexpr int STEP = kSmThreads * U;
   const int row = blockIdx.x;
   const float* xr = x + (size_t)row * cols;
@@ -452,12 +471,13 @@ hipError_t launch_softmax_rows(const float* x, float* y, int rows, int cols, hip
   if (vec && kSoftmaxWavePerRow && cols / 4 <= 64 * 16 && rows >= 16 * 256) {
     const int nacc = cols / 4;
     const dim3 wgrid((rows + kSmWaves - 1) / kSmWaves);
+    const dim3 wgrid2(((rows + 1) / 2 + kSmWaves - 1) / kSmWaves);
     if (nacc <= 64 * 4)
-      hipLaunchKernelGGL((softmax_rows_wave_kernel<4>), wgrid, block, 0, stream, x, y, rows, cols);
+      hipLaunchKernelGGL((softmax_rows_wave_kernel<4, 1>), wgrid, block, 0, stream, x, y, rows, cols);
     else if (nacc <= 64 * 8)
-      hipLaunchKernelGGL((softmax_rows_wave_kernel<8>), wgrid, block, 0, stream, x, y, rows, cols);
+      hipLaunchKernelGGL((softmax_rows_wave_kernel<8, 1>), wgrid, block, 0, stream, x, y, rows, cols);
     else
-      hipLaunchKernelGGL((softmax_rows_wave_kernel<16>), wgrid, block, 0, stream, x, y, rows, cols);
+      hipLaunchKernelGGL((softmax_rows_wave_kernel<16, 2>), wgrid2, block, 0, stream, x, y, rows, cols);
   } else if (vec) {
     const int nacc = cols / 4;
     if (nacc <= 256)

@@ -23,8 +23,9 @@ def _run_rows(x_np):
 @pytest.mark.parametrize("rows,cols", [
     (1, 1), (7, 3), (5, 4), (33, 1000), (17, 1001), (64, 4000), (8, 8192), (3, 8196),
     (4, 8193), (3, 20000), (2, 100003), (300, 63), (2, 1024), (2, 4096), (2, 4097),
-    # 4096 rows or more: one wave per row for rows of up to 4096 aligned floats
-    (4097, 4), (4099, 1000), (4100, 2000), (4097, 4096), (4096, 4100),
+    # 4096 rows or more: one wave per row for rows of up to 2048 aligned floats, one wave per two rows
+    # (rows g and g + ceil(rows / 2)) up to 4096; odd row counts leave the last wave one row
+    (4097, 4), (4099, 1000), (4100, 2000), (4097, 4096), (4099, 2052), (4096, 4100),
 ])
 def test_softmax_rows_parity(rows, cols):
     print(f"softmax_rows rows={rows} cols={cols}", flush=True)
