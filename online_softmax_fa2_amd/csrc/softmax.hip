@@ -246,8 +246,9 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_stream_kernel(const f
 // probabilities exp(x - m) / d.
 // ---------------------------------------------------------------------------
 
+// (Bitwise operators: no short-circuit branches in per-lane uses.)
 __device__ __forceinline__ bool better(float xa, int ia, float xb, int ib) {
-  return xa > xb || (xa == xb && ia < ib);
+  return (xa > xb) | ((xa == xb) & (ia < ib));
 }
 // Float order as signed-int order (for LDS integer max), and back.
 __device__ __forceinline__ int ord_f(float f) {
@@ -314,31 +315,39 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
   __shared__ float lm_s[kSmThreads];  // lane maxima of the first chunk
   __shared__ float qv_s[kSmWaves][kQueue];
   __shared__ int qi_s[kSmWaves][kQueue];
+  // The candidate and the threshold are wave-uniform: they are taken through
+  // readfirstlane so that the compiler keeps them in scalar registers and
+  // branches on them without exec-mask bookkeeping, and the next
+  // candidate's LDS read is issued before the current one is inserted.
+  auto uni = [](float f) { return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, f))); };
   auto drain = [&](int n) {
+    float nx = n > 0 ? qv_s[w][0] : 0.0f;
+    int ni = n > 0 ? qi_s[w][0] : 0;
     for (int q = 0; q < n; ++q) {
-      const float cx = qv_s[w][q];
-      const int ci = qi_s[w][q];
+      const float cx = uni(nx);
+      const int ci = __builtin_amdgcn_readfirstlane(ni);
+      if (q + 1 < n) {
+        nx = qv_s[w][q + 1];
+        ni = qi_s[w][q + 1];
+      }
       if (!better(cx, ci, Tx, Ti) && !(cx == Tx && Ti == 0x7fffffff)) continue;  // wave-uniform
       // Insert: lanes whose entry is worse than the candidate take the
       // previous lane's entry, or the candidate if the previous is better.
       const bool mine = better(cx, ci, lx, li);
       const float px = dpp_f<0x111>(kNegInf, lx);  // lane i - 1 (row 0 holds the list)
       const int pi = dpp_i<0x111>(0x7fffffff, li);
-      const bool prev_better = lane > 0 && better(px, pi, cx, ci);
-      if (mine && lane < 16) {
-        if (lane == 0 || prev_better) {
-          lx = cx;
-          li = ci;
-        } else {
-          lx = px;
-          li = pi;
-        }
-      }
+      const bool prev_better = (lane > 0) & better(px, pi, cx, ci);
+      const bool take = mine & (lane < 16);
+      const bool use_c = lane == 0 || prev_better;
+      const float ex = use_c ? cx : px;
+      const int ei = use_c ? ci : pi;
+      lx = take ? ex : lx;
+      li = take ? ei : li;
       const float kx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lx), k - 1));
       const int ki = __builtin_amdgcn_readlane(li, k - 1);
       if (better(kx, ki, Tx, Ti) || (kx == Tx && Ti == 0x7fffffff && ki != 0x7fffffff)) {
-        Tx = kx;
-        Ti = ki;
+        Tx = uni(kx);
+        Ti = __builtin_amdgcn_readfirstlane(ki);
       }
     }
   };
