@@ -236,12 +236,14 @@ __global__ __launch_bounds__(kSmThreads) void softmax_rows_stream_kernel(const f
 // Each wave keeps its current top-k candidates in lanes 0..k-1 (lane i holds
 // the i-th best; order: larger x first, lower column index on equal x) and a
 // wave-uniform threshold (Tx, Ti): an element can only enter the list if it
-// beats the threshold.  The threshold starts as the k-th largest of the 64
-// lanes' maxima over the wave's first chunk (a lower bound of the wave's
-// final k-th value: those k lane maxima are k distinct elements), so even
-// the first chunk offers only a handful of candidates; later it is the
-// list's k-th entry.  Candidates are inserted one at a time (readlane to
-// broadcast, a one-lane DPP shift of the list).  At the end the 4 waves'
+// beats the threshold.  The threshold starts as the k-th largest of the 256
+// lanes' maxima over the workgroup's first chunk (a lower bound of the row's
+// k-th value: those k lane maxima are k distinct elements), so even the
+// first chunk offers only a handful of candidates; later it is the largest
+// of the wave's k-th entry and the other waves' published ones (a wave's own
+// bound alone measured slower: more candidates).  Candidates are inserted
+// one at a time (readlane to broadcast, a one-lane DPP shift of the list).
+// At the end the 4 waves'
 // lists are ranked in LDS and the k best are written with their
 // probabilities exp(x - m) / d.
 // ---------------------------------------------------------------------------
@@ -353,11 +355,13 @@ __global__ __launch_bounds__(kSmThreads) void softmax_topk_kernel(const float* x
   };
 
   auto process = [&](int base, float (&v)[U][W]) {
+    if (base + STEP > nacc) {  // the row's last chunk (wave-uniform)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = base + threadIdx.x + kSmThreads * u < nacc;
+      for (int u = 0; u < U; ++u) {
+        const bool ok = base + threadIdx.x + kSmThreads * u < nacc;
 #pragma unroll
-      for (int e = 0; e < W; ++e) v[u][e] = ok ? v[u][e] : kNegInf;
+        for (int e = 0; e < W; ++e) v[u][e] = ok ? v[u][e] : kNegInf;
+      }
     }
     float mx = kNegInf;
 #pragma unroll
