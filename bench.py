@@ -313,7 +313,7 @@ def main():
             "attn_fwd_f32_n1000": {"workload": c1_name, "avg_us": round(ms["attn_fwd_f32_n1000"] * 1e3, 2),
                                    "min_us": round(ms_min["attn_fwd_f32_n1000"] * 1e3, 2),
                                    "tflops": round(c1_tflops, 3), "algorithmic_flop": c1_flops,
-                                   "bound": "latency (one head of 1000 queries: 8 query tiles)"},
+                                   "bound": "latency (one head of 1000 queries: 63 workgroups of 16 queries on 256 CUs)"},
             "attn_bwd": {"workload": fw_name, "avg_us": round(ms["attn_bwd"] * 1e3, 2),
                          "min_us": round(ms_min["attn_bwd"] * 1e3, 2), "tflops": round(bwd_tflops, 2),
                          "frac_mfma_peak": round(bwd_tflops / acc.PEAK_BF16_TFLOPS, 4),

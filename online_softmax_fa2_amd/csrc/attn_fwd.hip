@@ -1127,6 +1127,172 @@ __global__ __launch_bounds__(64 * S, 1) void fwd_f32_split_kernel(FwdParams p) {
 }
 
 
+// ---------------------------------------------------------------------------
+// float32, smallest launches: 16-query workgroups on v_mfma_f32_16x16x4_f32.
+//
+// The key-split kernel above runs one 32-query tile per workgroup; a single
+// head of 1000 queries is then 32 workgroups, and their matrix time (the
+// per-CU MFMA work is fixed by the tile) sets the launch's time.  With 16
+// queries per workgroup the same work spreads over twice as many CUs at the
+// same MFMA rate per query-key pair.  Structure as above: S waves take the
+// 16-key blocks of the range in turn, each keeps its own (m, l, O), and the
+// partial states are merged through LDS by the split-KV rescale rule.
+//
+// Layouts (lane l, g = l / 16, c = l % 16): an MFMA step takes A[c][g],
+// B[g][c] and leaves D[4 g + i][c] in register i.  Scores are S^T = K Q^T
+// with the K rows permuted (A row r holds key 4 (r % 4) + r / 4), so that
+// register i of lane l holds key 4 i + g of query c: exactly the B operand
+// of P V step i (keys 4 i .. 4 i + 3), with no data movement.
+// ---------------------------------------------------------------------------
+template <int D, int S>
+__global__ __launch_bounds__(64 * S, 1) void fwd_f32_split16_kernel(FwdParams p) {
+  constexpr int BC = 16;       // keys per block
+  constexpr int RK = D + 4;    // K row stride (floats): an S step's 16 rows x 4 columns hit 64 distinct banks
+  constexpr int RV = D + 16;   // V row stride: a P V step's 4 rows x 16 columns hit 64 distinct banks
+  constexpr int NKK = D / 4;   // S steps (4 d each)
+  constexpr int NMD = D / 16;  // 16-row d tiles of O^T
+  constexpr int WREG = BC * RK + BC * RV;  // floats of one wave's region (K rows, then V rows)
+  static_assert(32 + 16 * D <= WREG, "the merge state fits in a wave's region");
+  __shared__ __attribute__((aligned(16))) float lds[S * WREG];
+
+  const Tile tile = map_tile(p);
+  if (!tile.valid) return;
+  const int b = tile.bh / p.H;
+  const int q0 = tile.q0;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+  const int N = p.N;
+  const size_t head_off = (size_t)tile.bh * (size_t)N * D;
+  const float* Kg = static_cast<const float*>(p.k) + head_off;
+  const float* Vg = static_cast<const float*>(p.v) + head_off;
+
+  const int qi = q0 + c16;
+  float qreg[NKK];  // Q[qi][4 kk + g]
+  {
+    const bool ok = qi < N;
+    const float* src = static_cast<const float*>(p.q) + head_off + (size_t)(ok ? qi : 0) * D + g;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qreg[kk] = ok ? src[4 * kk] : 0.0f;
+  }
+
+  const KeyRange kr = key_range(p, b, q0);
+  const KeySpan span = key_span(p, kr.jmax, qi);
+  const int kb_lo = kr.kbeg / BC;
+  const int kb_hi = (kr.kend > kr.kbeg) ? (kr.kend + BC - 1) / BC : kb_lo;
+  float* ks = lds + w * WREG;
+  float* vs = ks + BC * RK;
+  const int krow = 4 * (c16 & 3) + (c16 >> 2);  // the key this lane feeds as A row c16
+
+  f32x4 oacc[NMD];
+#pragma unroll
+  for (int md = 0; md < NMD; ++md) oacc[md] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = kNegInf, l_run = 0.0f;
+  const float c = p.c;
+
+  // K and V rows of a block pass through registers on their way to the
+  // wave's LDS region; the next block's are loaded while the current one is
+  // computed.  Lane `lane` holds the 16-byte chunks lane + 64 t of the
+  // block (rows past N read row N - 1; they are masked).
+  constexpr int NLD = BC * D / 4 / 64;
+  f32x4 kbuf[NLD], vbuf[NLD];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int idx = lane + 64 * t;
+      const int row = idx / (D / 4), c4 = idx % (D / 4);
+      const int j = min(kb * BC + row, N - 1);
+      kbuf[t] = *reinterpret_cast<const f32x4*>(Kg + (size_t)j * D + 4 * c4);
+      vbuf[t] = *reinterpret_cast<const f32x4*>(Vg + (size_t)j * D + 4 * c4);
+    }
+  };
+  if (kb_lo + w < kb_hi) fetch(kb_lo + w);
+  for (int kb = kb_lo + w; kb < kb_hi; kb += S) {
+    const int j0 = kb * BC;
+    // Other lanes read the previous block's rows from this region: the
+    // writes wait for those reads, and the reads below for the writes.
+    wave_sync();
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int idx = lane + 64 * t;
+      const int row = idx / (D / 4), c4 = idx % (D / 4);
+      *reinterpret_cast<f32x4*>(ks + row * RK + 4 * c4) = kbuf[t];
+      *reinterpret_cast<f32x4*>(vs + row * RV + 4 * c4) = vbuf[t];
+    }
+    wave_sync();
+    if (kb + S < kb_hi) fetch(kb + S);
+    f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float* kr_row = ks + krow * RK + g;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x4f32(kr_row[4 * kk], qreg[kk], s, 0, 0, 0);
+    // Masks by selects on every block (no branch between the MFMAs and the
+    // first read of their result).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 4 * i + g;
+      s[i] = (j < span.lo || j > span.hi) ? kNegInf : s[i];
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // the block's maximum for query c16
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_ref = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    float rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(fmaf(s[i], c, -m_ref));
+      s[i] = e;
+      rs += e;
+    }
+    l_run = l_run * alpha + rs;  // this lane's keys only; summed over g at the end
+    m_run = m_new;
+#pragma unroll
+    for (int md = 0; md < NMD; ++md) oacc[md] *= alpha;
+    // O^T += V^T P^T: step i takes keys 4 i .. 4 i + 3 (A[c][g] = V[4 i + g][16 md + c]).
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+        oacc[md] = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[(4 * i + g) * RV + 16 * md + c16], s[i], oacc[md], 0, 0, 0);
+  }
+
+  // This wave's state into its region: m[16], l[16], O[16][D] (query-major).
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  float* st = ks;
+  if (g == 0) {
+    st[c16] = m_run;
+    st[16 + c16] = l_tot;
+  }
+#pragma unroll
+  for (int md = 0; md < NMD; ++md)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[32 + c16 * D + 16 * md + 4 * g + i] = oacc[md][i];
+  __syncthreads();
+  // Merge: thread t takes elements t, t + 64 S, ... of the tile's 16 x D outputs.
+  for (int e = threadIdx.x; e < 16 * D; e += 64 * S) {
+    const int q = e / D, d = e % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < S; ++u) M = fmaxf(M, lds[u * WREG + q]);
+    float lsum = 0.0f, osum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const float mu = lds[u * WREG + q];
+      const float wgt = (mu == kNegInf) ? 0.0f : fast_exp2(mu - M);
+      lsum += wgt * lds[u * WREG + 16 + q];
+      osum += wgt * lds[u * WREG + 32 + q * D + d];
+    }
+    const int qq = q0 + q;
+    if (qq < N) {
+      static_cast<float*>(p.o)[head_off + (size_t)qq * D + d] = lsum > 0.0f ? osum / lsum : 0.0f;
+      if (d == 0) p.lse[(size_t)tile.bh * N + qq] = lsum > 0.0f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
@@ -1153,10 +1319,20 @@ hipError_t launch_attn_fwd_bf16_exp2_offload(const FwdArgs& a, int poly_every, h
 }
 
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream) {
-  // Fewer 128-query tiles than CUs: 32-query workgroups whose waves split the
-  // keys (8 waves at d = 64; 4 at d = 128, whose per-wave K and V regions
-  // take 33 KB of LDS each).
+  // Fewer 32-query tiles than CUs: 16-query workgroups of 8 waves that split
+  // the keys.  Fewer 128-query tiles than CUs: 32-query workgroups whose
+  // waves split the keys (8 waves at d = 64; 4 at d = 128, whose per-wave K
+  // and V regions take 33 KB of LDS each).
   const long long tiles128 = (long long)a.B * a.H * ((a.N + kBr - 1) / kBr);
+  const long long tiles32 = (long long)a.B * a.H * ((a.N + 31) / 32);
+  if (tiles32 < kSplitTilesBelow) {
+    const FwdParams p = make_params(a, 16);
+    if (a.d == 128)
+      hipLaunchKernelGGL((fwd_f32_split16_kernel<128, 8>), dim3(grid_for(p)), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_f32_split16_kernel<64, 8>), dim3(grid_for(p)), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
   if (tiles128 < kSplitTilesBelow) {
     const FwdParams p = make_params(a, 32);
     if (a.d == 128)

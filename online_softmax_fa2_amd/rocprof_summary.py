@@ -32,6 +32,7 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h"],
     "fwd_f32_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h"],
     "fwd_f32_split_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h"],
+    "fwd_f32_split16_kernel": ["csrc/attn_fwd.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h"],
     "fwd_fp8_d128_kernel": ["csrc/attn_fwd_fp8.hip", "csrc/fwd_common.h", "csrc/masks.h", "csrc/device_common.h",
                             "csrc/tile_layout.h"],
     "decode_partial_kernel": ["csrc/decode.hip", "csrc/device_common.h"],
@@ -52,7 +53,7 @@ def short_name(name: str) -> str:
     m = re.search(r"decode_partial_kernelI(DF16b|f)Li(\d+)E", name)
     if m:
         return f"decode_partial_kernel<{'bf16' if m.group(1) == 'DF16b' else 'f32'}, {m.group(2)}>"
-    m = re.search(r"(fwd_bf16_d128_kernel<[^>]*>|fwd_bf16_kernel<\d+>|fwd_f32_kernel<\d+>|fwd_f32_split_kernel<[^>]*>|"
+    m = re.search(r"(fwd_bf16_d128_kernel<[^>]*>|fwd_bf16_kernel<\d+>|fwd_f32_kernel<\d+>|fwd_f32_split_kernel<[^>]*>|fwd_f32_split16_kernel<[^>]*>|"
                   r"decode_partial_kernel\w*|decode_merge_kernel<\d+>|softmax_topk_kernel<\d, (?:true|false)>|"
                   r"softmax_rows_\w+<[\d, ]+>|bwd_dkdv_kernel(?:<\w+>)?|bwd_dq_kernel|bwd_dqs_kernel|bwd_prep_kernel|fwd_fp8_d128_kernel|"
                   r"__amd_rocclr_copyBuffer|copyBuffer)", name)

@@ -186,10 +186,26 @@ def test_fwd_exp2_offload_full_window_pad_8192():
 ])
 def test_fwd_f32_tile_path(B, H, N, d, causal, window, kv_len):
     """float32 launches with at least 256 tiles of 128 queries take the 128-query tile kernel; launches with
-    fewer take the key-split kernel, which the other float32 cases here run (d = 64 and d = 128)."""
+    fewer take a key-split kernel: 32-query workgroups (test_fwd_f32_split32_path), or 16-query ones when
+    there are fewer than 256 tiles of 32 queries, which the other float32 cases here run (d = 64 and 128)."""
     assert B * H * ((N + 127) // 128) >= 256
     print(f"attn_fwd f32 tile path B={B} H={H} N={N} d={d}", flush=True)
     inp = attn_inputs(B, H, N, d, dtype="f32", seed=N + d, causal=causal, window=window, kv_len=kv_len)
+    O, L = run_fwd(inp)
+    check(inp, O, L, heads=[(0, 0), (B - 1, H - 1), (0, H // 2)])
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,window,kv_len", [
+    (1, 16, 600, 64, True, 200, None),
+    (1, 8, 1100, 128, False, 0, [900]),
+    (2, 5, 833, 64, False, 100, [833, 17]),
+])
+def test_fwd_f32_split32_path(B, H, N, d, causal, window, kv_len):
+    """float32 launches with fewer than 256 tiles of 128 queries but at least 256 of 32 take the key-split
+    kernel with 32-query workgroups."""
+    assert B * H * ((N + 127) // 128) < 256 <= B * H * ((N + 31) // 32)
+    print(f"attn_fwd f32 split32 path B={B} H={H} N={N} d={d}", flush=True)
+    inp = attn_inputs(B, H, N, d, dtype="f32", seed=N + 3 * d, causal=causal, window=window, kv_len=kv_len)
     O, L = run_fwd(inp)
     check(inp, O, L, heads=[(0, 0), (B - 1, H - 1), (0, H // 2)])
 
