@@ -8,10 +8,12 @@
 // a top-k list next to (m, d) during the single pass and outputs only the k
 // probabilities and their column indices (Step 3, fusion with top-k).
 //
-// gfx950 mapping: one 256-thread workgroup per row.  Each lane folds its
-// elements into its own (m, d) a chunk at a time (chunk maximum, one rescale
-// of d, one exp2 per element with log2(e) folded into an FMA), then the 64
-// lanes of a wave merge by butterfly exchanges and the 4 waves through LDS.
+// gfx950 mapping: one 256-thread workgroup per row, or, when at least 4096
+// rows of at most 4096 aligned floats fill the chip, one wave per row (per
+// two rows above 2048 floats).  Each lane folds its elements into its own
+// (m, d) a chunk at a time (chunk maximum, one rescale of d, one exp2 per
+// element with log2(e) folded into an FMA), then the 64 lanes of a wave
+// merge by butterfly exchanges and the waves of a workgroup through LDS.
 // Rows of up to 8192 columns are held in registers between the passes, so
 // HBM sees one read and one write per element; longer rows re-read x.
 // Accesses are float4 (16 B per lane, fully coalesced) when the row length
