@@ -262,3 +262,35 @@ def test_fwd_bf16_largest_offsets():
         what = f"h={h} rows {s}..{s + M - 1}"
         assert_bf16_out(og, Or[0, 0], what=what + " O")
         assert_lse_abs(lg, Lr[0, 0], 1e-3, what=what + " LSE")
+
+
+def _sweep_configs(n=16, seed=20261202):
+    """Seeded random forward configurations: sizes from 1 to ~900 queries (log-uniform), both head
+    dimensions, causal or not, a window on half of them, per-batch padding on some, planted large keys on
+    some. Every launch path of attn_fwd's small sizes is drawn (FP32: the 16-query split kernel; bf16: the
+    d = 64 and d = 128 tile kernels)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        N = int(np.clip(np.exp(rng.uniform(0, np.log(900))), 1, 900))
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        window = int(rng.integers(1, N + 40)) if rng.uniform() < 0.5 else 0
+        kv_len = [int(x) for x in rng.integers(0, N + 1, size=B)] if rng.uniform() < 0.4 else None
+        big = int(rng.integers(0, min(N, 4) + 1))
+        out.append((B, H, N, d, causal, window, kv_len, big))
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cfg", _sweep_configs(), ids=[f"s{i}" for i in range(16)])
+def test_fwd_random_sweep(dtype, cfg):
+    """Every head of every drawn configuration against the oracle, element by element, at the dtype's bar."""
+    B, H, N, d, causal, window, kv_len, big = cfg
+    print(f"attn_fwd sweep {dtype} B={B} H={H} N={N} d={d} causal={causal} window={window} kv_len={kv_len} "
+          f"big={big}", flush=True)
+    inp = attn_inputs(B, H, N, d, dtype=dtype, seed=N * 7 + d + B, causal=causal, window=window, kv_len=kv_len,
+                      n_big_keys=big)
+    O, L = run_fwd(inp)
+    check(inp, O, L)
