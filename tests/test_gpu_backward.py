@@ -127,6 +127,35 @@ def test_bwd_parity(case, stored):
     check(inp, do, got)
 
 
+def _sweep_cases(n=10, seed=20261203):
+    """Seeded random backward configurations (d = 128): 1 to ~700 queries (log-uniform), causal or not, a
+    window on half of them, per-batch padding (possibly 0) on some, planted large keys on some."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        N = int(np.clip(np.exp(rng.uniform(0, np.log(700))), 1, 700))
+        causal = bool(rng.integers(0, 2))
+        window = int(rng.integers(1, N + 40)) if rng.uniform() < 0.5 else 0
+        kv_len = [int(x) for x in rng.integers(0, N + 1, size=B)] if rng.uniform() < 0.4 else None
+        out.append((B, H, N, causal, window, kv_len, int(rng.integers(0, min(N, 4) + 1))))
+    return out
+
+
+@pytest.mark.parametrize("stored", [True, False], ids=["stored_ds", "recompute"])
+@pytest.mark.parametrize("case", _sweep_cases(), ids=[f"s{i}" for i in range(10)])
+def test_bwd_random_sweep(case, stored):
+    """Every head of every drawn configuration against the oracle's gradients, within the bound."""
+    B, H, N, causal, window, kv_len, nbig = case
+    print(f"attn_bwd sweep B={B} H={H} N={N} causal={causal} window={window} kv_len={kv_len} big={nbig} "
+          f"stored={stored}", flush=True)
+    inp = attn_inputs(B, H, N, 128, dtype="bf16", seed=N * 5 + B, causal=causal, window=window, kv_len=kv_len,
+                      n_big_keys=nbig)
+    do_bits, do = grad_inputs(B, H, N, 128, seed=N + 11)
+    got = run_fwd_bwd(inp, do_bits, stored)
+    check(inp, do, got)
+
+
 @pytest.mark.parametrize("case", [CASES[7], CASES[8], CASES[12]], ids=["window_pad", "noncausal_window", "wide"])
 def test_bwd_paths_agree(case):
     """dK and dV come from the same kernel either way (identical); dQ from the stored dS or from recomputed S and
