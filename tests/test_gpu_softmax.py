@@ -109,6 +109,30 @@ def test_topk_parity(rows, cols, k):
     assert_f32_rel(tv, rv, what="top-k values")
 
 
+@pytest.mark.parametrize("order", ["ascending", "descending", "plateau", "random"])
+@pytest.mark.parametrize("cols,k", [(5000, 5), (2051, 16), (777, 3)])
+def test_topk_structured_rows(order, cols, k):
+    """Rows whose order stresses the candidate handling: ascending (every element beats the running
+    threshold, so every chunk fills the candidate queue), descending (only the first chunk offers any),
+    a plateau of equal maxima spread over the row, and random; aligned and unaligned row lengths."""
+    rng = np.random.default_rng(cols + k)
+    rows = 6
+    if order == "ascending":
+        x = np.tile(np.linspace(-5.0, 5.0, cols, dtype=np.float32), (rows, 1))
+    elif order == "descending":
+        x = np.tile(np.linspace(5.0, -5.0, cols, dtype=np.float32), (rows, 1))
+    elif order == "plateau":
+        x = rng.normal(0.0, 1.0, (rows, cols)).astype(np.float32)
+        x[:, rng.choice(cols, size=min(cols, 3 * k), replace=False)] = 9.0
+    else:
+        x = rng.normal(0.0, 4.0, (rows, cols)).astype(np.float32)
+    print(f"topk structured {order} cols={cols} k={k}", flush=True)
+    tv, ti, _ = _run_topk(x, k)
+    rv, ri = topk_ref(x, k)
+    assert np.array_equal(ti, ri), "top-k indices differ"
+    assert_f32_rel(tv, rv, what=f"top-k values ({order})")
+
+
 def test_topk_ties_take_lower_index():
     rng = np.random.default_rng(5)
     x = rng.integers(-3, 4, size=(32, 3000)).astype(np.float32)  # massive ties
